@@ -1,0 +1,83 @@
+"""Readers for the golden pin files and builders of the exact-input cases.
+
+These helpers only parse text and place values into input arrays; they hold
+none of the method's arithmetic.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+from iso_synth import f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _value(tok: str) -> float:
+    tok = tok.strip()
+    neg = tok.startswith("-")
+    if neg:
+        tok = tok[1:]
+    if tok.startswith("2^"):
+        v = 2.0 ** int(tok[2:])
+    else:
+        v = float(int(tok))
+    return -v if neg else v
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                yield [c.strip() for c in line.split("|")]
+
+
+def tree_pins():
+    """Rows of tree_order_pins.txt as dicts."""
+    out = []
+    for kind, leaves, vals, bal, seq, other in _lines("tree_order_pins.txt"):
+        name, bits = other.split("=")
+        out.append(dict(kind=kind, leaves=int(leaves), values=[_value(v) for v in vals.split()],
+                        balanced=int(bal, 16), sequential=int(seq, 16),
+                        other_name=name, other=int(bits, 16)))
+    return out
+
+
+def logsoftmax_forms():
+    return [dict(V=int(v), case=c, expected=float(e))
+            for v, c, e in _lines("logsoftmax_closed_forms.txt")]
+
+
+def product_factors(v: float):
+    """Two bf16-exact factors whose product is exactly v (v in {0, +-1, +-2^-2j})."""
+    if v == 0.0:
+        return 0.0, 0.0
+    mant, exp = np.frexp(abs(v))  # v = mant * 2^exp, mant = 0.5 for powers of two
+    assert mant == 0.5, "pins use powers of two"
+    e = int(exp) - 1
+    assert e % 2 == 0
+    return float(np.copysign(2.0 ** (e // 2), v)), 2.0 ** (e // 2)
+
+
+def tree_case_inputs(pin, leaf_size: int, rows: int = 1, cols: int = 1, kind=None):
+    """A [rows][K] and Wt [cols][K] bf16 bits such that every output element
+    has, for a "tree" pin, exactly one product per leaf equal to the pin's leaf
+    value; for an "inleaf" pin, the values sit in consecutive k of leaf 0."""
+    kind = kind or pin["kind"]
+    L = pin["leaves"]
+    K = L * leaf_size
+    a = np.zeros(K, dtype=np.float32)
+    w = np.zeros(K, dtype=np.float32)
+    for i, v in enumerate(pin["values"]):
+        k = i * leaf_size + (i * 7) % leaf_size if kind == "tree" else i
+        fa, fw = product_factors(v)
+        a[k], w[k] = fa, fw
+    A = np.tile(f32_to_bf16_bits(a), (rows, 1))
+    Wt = np.tile(f32_to_bf16_bits(w), (cols, 1))
+    return A, Wt
+
+
+def f32_bits(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).view(np.uint32)
