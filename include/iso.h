@@ -1,0 +1,197 @@
+/*
+ * iso.h -- C ABI of the parallelism- and batch-invariant matmul and
+ * token-logprob library for AMD MI355X (gfx950).
+ *
+ * Pages cited (web pages about IsoExec):
+ *   [AGL] "IsoExec: Eliminating Trainer-Inference Mismatch in SkyRL"
+ *         (agentlenshq.com blog summary)
+ *   [KTB] katelyatop-blog.pages.dev post on vLLM/SkyRL IsoExec and the
+ *         trainer-inference mismatch (numbered sections)
+ *   [DDV] "IsoExec: Unified Execution to Eliminate Trainer-Inference
+ *         Mismatch in SkyRL" (daily.dev summary)
+ *
+ * Numerics common to every entry point.  A contraction over K is cut into
+ * `leaf_count` contiguous leaves of `leaf_size`; each leaf is a bf16 dot
+ * product accumulated in FP32 with one fixed MFMA schedule; the leaf sums are
+ * combined by the balanced binary tree in leaf-index order (pairs (2i, 2i+1)
+ * at every level) ([AGL] "Achieving Parallelism Invariance", TP bullet;
+ * [KTB] section 8).  The bits of an output element therefore depend only on
+ * its own input row, its own weight column and the contract -- not on the
+ * batch size, the row's position in the batch, the tiling, or the number of
+ * partitions ("emulated ranks") the leaves are spread over ([AGL] "Contract
+ * Structure and Enforcement": composition pins the reduction decomposition,
+ * claims list the parallel sizes for which the tree is proven invariant).
+ *
+ * Conventions.
+ *   - Memory: every tensor pointer is a DEVICE pointer owned by the caller,
+ *     row-major and contiguous.  bf16 tensors are raw 16-bit patterns.
+ *     Weights are stored k-contiguous: a K x N matrix W is passed as its
+ *     transpose Wt [N][K] (the storage of a linear layer's weight).
+ *   - Workspace: the caller passes device scratch of at least the size the
+ *     matching *_workspace() function returns (may be 0 / NULL when that
+ *     size is 0).  The library allocates and frees nothing.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *     only enqueued; nothing synchronises.  No global mutable state: calls are
+ *     thread-safe; calls that share a workspace must be ordered by the caller.
+ *   - Errors: every argument, shape, dtype, claim and workspace check runs on
+ *     the host before anything is launched; on error nothing is written and
+ *     no HIP call is made.  ISO_ERR_LAUNCH reports a failed launch; device
+ *     faults surface at the caller's next synchronisation.
+ *   - Sizes are int64_t; M, N, K, V, T >= 0; an empty problem (M == 0 or
+ *     N == 0) returns ISO_OK without launching.
+ */
+#ifndef ISO_H_
+#define ISO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ISO_ABI_VERSION 1u
+
+typedef enum iso_status {
+    ISO_OK = 0,
+    ISO_ERR_ARG = 1,        /* null pointer, bad enum value, negative size */
+    ISO_ERR_SHAPE = 2,      /* K != leaf_count * leaf_size, size limits exceeded */
+    ISO_ERR_DTYPE = 3,      /* unsupported input / accumulation / output dtype */
+    ISO_ERR_CLAIM = 4,      /* partition count outside the contract's claims */
+    ISO_ERR_IDENTITY = 5,   /* contract digest differs from the expected one */
+    ISO_ERR_WORKSPACE = 6,  /* workspace missing or too small */
+    ISO_ERR_LAUNCH = 7,     /* a kernel launch failed */
+    ISO_ERR_CONTRACT = 8    /* malformed contract (version, leaf shape, tree, schedule) */
+} iso_status;
+
+/* dtypes */
+#define ISO_BF16 1u
+#define ISO_F32 2u
+
+/* tree: the balanced binary tree over leaf index, lower index on the left */
+#define ISO_TREE_BALANCED 1u
+/* schedule: bf16 MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16), FP32 accumulator,
+ * K ascending in steps of 32 inside each leaf; the leaf sum starts at +0.0 */
+#define ISO_SCHED_MFMA16X16X32_KASC 1u
+
+/* Vocabulary chunk width of the LM-head softmax (its leaf size). */
+#define ISO_VOCAB_CHUNK 128u
+
+/*
+ * The numerical-policy part of an execution contract, one per region (one
+ * kernel-implemented arithmetic span: gemm, lmhead, moe gate/up, moe down)
+ * ([AGL] "Contract Structure and Enforcement": regions, composition with
+ * pinned accumulation dtype and reduction-decomposition parameters).
+ *   abi_version  ISO_ABI_VERSION
+ *   in_dtype     ISO_BF16 (only)
+ *   accum_dtype  ISO_F32 (only)
+ *   leaf_count   L: power of two, 1..64
+ *   leaf_size    m: multiple of 64, 64..65536; K must equal L * m
+ *   tree         ISO_TREE_BALANCED (only)
+ *   vocab_chunk  ISO_VOCAB_CHUNK for iso_lmhead_logprob, 0 otherwise
+ *   schedule     ISO_SCHED_MFMA16X16X32_KASC (only)
+ */
+typedef struct iso_contract {
+    uint32_t abi_version;
+    uint32_t in_dtype;
+    uint32_t accum_dtype;
+    uint32_t leaf_count;
+    uint32_t leaf_size;
+    uint32_t tree;
+    uint32_t vocab_chunk;
+    uint32_t schedule;
+} iso_contract;
+
+/* Fill *c with the defaults above and the given leaf shape and vocab chunk.
+ * Returns ISO_ERR_ARG for a NULL pointer; the result is not validated. */
+iso_status iso_contract_init(iso_contract *c, uint32_t leaf_count, uint32_t leaf_size,
+                             uint32_t vocab_chunk);
+
+/* ISO_OK if *c is well formed (see the field list), else ISO_ERR_CONTRACT
+ * (ISO_ERR_DTYPE for an unsupported dtype, ISO_ERR_ARG for NULL). */
+iso_status iso_contract_validate(const iso_contract *c);
+
+/*
+ * numerical_policy identity ([AGL] "Contract Structure and Enforcement",
+ * identities; [KTB] section 6, the contract digest as a lockfile):
+ * out[32] = SHA-256 (FIPS 180-4) of the 24-byte tag
+ * "iso.numerical_policy.v1" followed by one NUL byte, then the eight uint32
+ * fields above in declaration order, little-endian (56 bytes in all).
+ * The contract must validate first.  Host only; never touches the GPU.
+ */
+iso_status iso_contract_digest(const iso_contract *c, uint8_t out[32]);
+
+/* ISO_OK if the digest of *c equals want[32], ISO_ERR_IDENTITY otherwise. */
+iso_status iso_contract_check(const iso_contract *c, const uint8_t want[32]);
+
+/*
+ * Topology claim ([AGL] "Contract Structure and Enforcement", claims): a
+ * contract with L leaves is proven partition-invariant for P in {1, 2, 4, 8}
+ * with P dividing L.  Partition p owns the contiguous leaf block
+ * [p*L/P, (p+1)*L/P), a whole subtree ([AGL] TP bullet: the contract fixes
+ * the rank-to-leaf map).  Returns ISO_OK or ISO_ERR_CLAIM.
+ */
+iso_status iso_check_partitions(const iso_contract *c, int partitions);
+
+/* Workspace bytes iso_gemm needs for this shape (0 when none); (size_t)-1
+ * for arguments iso_gemm would reject. */
+size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int partitions);
+
+/*
+ * Invariant GEMM ([AGL] "Achieving Parallelism Invariance", TP bullet):
+ *   C [M][N] = A [M][K] * W, W passed as Wt [N][K]; K = L * m.
+ *   out_dtype ISO_F32: C is FP32, the tree root.
+ *   out_dtype ISO_BF16: C is bf16, the FP32 root rounded to nearest-even.
+ * `partitions` P emulates P tensor-parallel ranks on this GPU: partition p
+ * computes its subtree root into the workspace and a combine kernel applies
+ * the top log2(P) levels.  Every P allowed by the claim gives the same bits.
+ * Limits: M, N < 2^23, K <= 2^22.
+ */
+iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *C,
+                    uint32_t out_dtype, int64_t M, int64_t N, int64_t K, int partitions,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Non-invariant comparison profile ([KTB] section 20, correctness versus
+ * performance profiles): the same tiles with ONE accumulator over all of K
+ * (no leaves, no tree).  Its bits match iso_gemm's only by accident; it
+ * exists to measure the cost of invariance.  Arguments as iso_gemm minus the
+ * contract and partitions.  K: multiple of 64.
+ */
+iso_status iso_gemm_baseline(const void *A, const void *Wt, void *C, uint32_t out_dtype,
+                             int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Workspace bytes iso_lmhead_logprob needs; (size_t)-1 for bad arguments. */
+size_t iso_lmhead_workspace(const iso_contract *c, int64_t M, int64_t V, int partitions);
+
+/*
+ * Sampled-token logprob ([KTB] section 1: the rollout records the sampled
+ * token's logprob and the trainer recomputes it; section 4: their ratio):
+ *   z = H [M][K] * W_vocab, W_vocab passed as Wvt [V][K], FP32 logits from
+ *       the same leaf/tree contraction as iso_gemm (never rounded to bf16,
+ *       never written to memory);
+ *   logprob[i] = z[i][t] - logsumexp(z[i][:]),  t = tok[i].
+ * The softmax reduction is itself a fixed tree: the vocabulary is cut into
+ * chunks of 128 ids; per chunk the max and the sum of exp(z - chunk max)
+ * are reduced over a balanced binary tree in index order, and the chunk
+ * pairs (m, s) are merged over the balanced tree in chunk order (padded with
+ * the identity (-inf, 0)) by (m, s) + (m', s') = (u, s e^(m-u) + s' e^(m'-u)),
+ * u = max(m, m').  c->vocab_chunk must be ISO_VOCAB_CHUNK.  A token id
+ * outside [0, V) gives NaN for its row.  Limits: 1 <= V <= 2^20, M < 2^31.
+ */
+iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *Wvt,
+                              const int32_t *tok, float *logprob, int64_t M, int64_t V,
+                              int64_t K, int partitions, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *iso_status_str(iso_status s);
+
+/* Library version string, e.g. "iso 0.1.0 gfx950". */
+const char *iso_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISO_H_ */

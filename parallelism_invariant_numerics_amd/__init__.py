@@ -1,0 +1,238 @@
+"""Python binding of libiso -- parallelism- and batch-invariant matmul and
+token-logprob kernels for AMD MI355X (gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels behind
+the C ABI declared in ``include/iso.h``.  PyTorch provides device memory and
+the current HIP stream.  bf16 operands are ``torch.bfloat16`` (or 16-bit
+integer tensors holding bf16 bit patterns); weights are stored k-contiguous,
+``Wt[N][K]`` for a K x N matrix.
+
+If ``libiso.so`` has not been built, importing this package raises
+``ImportError``; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "IsoError", "Contract", "contract", "digest", "check_identity", "check_partitions",
+    "gemm_workspace", "gemm", "gemm_baseline", "lmhead_workspace", "lmhead_logprob",
+    "lib", "LIB_PATH", "F32", "BF16", "VOCAB_CHUNK", "version",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libiso.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m parallelism_invariant_numerics_amd.build` "
+        "(the library has no non-HIP fallback)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+BF16 = 1
+F32 = 2
+VOCAB_CHUNK = 128
+_STATUS = {0: "ISO_OK", 1: "ISO_ERR_ARG", 2: "ISO_ERR_SHAPE", 3: "ISO_ERR_DTYPE",
+           4: "ISO_ERR_CLAIM", 5: "ISO_ERR_IDENTITY", 6: "ISO_ERR_WORKSPACE",
+           7: "ISO_ERR_LAUNCH", 8: "ISO_ERR_CONTRACT"}
+
+
+class Contract(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint32) for n in (
+        "abi_version", "in_dtype", "accum_dtype", "leaf_count", "leaf_size", "tree",
+        "vocab_chunk", "schedule")]
+
+    def __repr__(self):
+        return "Contract(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class IsoError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+        msg = lib.iso_status_str(status).decode()
+        super().__init__(f"{where}: {self.name} ({msg})")
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_U32 = ctypes.c_uint32
+_CP = ctypes.POINTER(Contract)
+_SIGS = {
+    "iso_contract_init": ([_CP, _U32, _U32, _U32], _I),
+    "iso_contract_validate": ([_CP], _I),
+    "iso_contract_digest": ([_CP, ctypes.c_char_p], _I),
+    "iso_contract_check": ([_CP, ctypes.c_char_p], _I),
+    "iso_check_partitions": ([_CP, _I], _I),
+    "iso_gemm_workspace": ([_CP, _I64, _I64, _I], ctypes.c_size_t),
+    "iso_gemm": ([_CP, _P, _P, _P, _U32, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P], _I),
+    "iso_gemm_baseline": ([_P, _P, _P, _U32, _I64, _I64, _I64, _P], _I),
+    "iso_lmhead_workspace": ([_CP, _I64, _I64, _I], ctypes.c_size_t),
+    "iso_lmhead_logprob": ([_CP, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P],
+                           _I),
+    "iso_status_str": ([_I], ctypes.c_char_p),
+    "iso_version": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+_BAD_SIZE = ctypes.c_size_t(-1).value
+
+
+def version() -> str:
+    return lib.iso_version().decode()
+
+
+def _ok(status: int, where: str):
+    if status != 0:
+        raise IsoError(status, where)
+
+
+def contract(leaf_count: int, leaf_size: int, vocab_chunk: int = 0) -> Contract:
+    """A validated contract with the library defaults (bf16 in, FP32
+    accumulation, balanced tree, MFMA 16x16x32 schedule)."""
+    c = Contract()
+    _ok(lib.iso_contract_init(ctypes.byref(c), leaf_count, leaf_size, vocab_chunk),
+        "iso_contract_init")
+    _ok(lib.iso_contract_validate(ctypes.byref(c)), "iso_contract_validate")
+    return c
+
+
+def digest(c: Contract) -> bytes:
+    """numerical_policy identity (SHA-256) of a contract."""
+    out = ctypes.create_string_buffer(32)
+    _ok(lib.iso_contract_digest(ctypes.byref(c), out), "iso_contract_digest")
+    return out.raw
+
+
+def check_identity(c: Contract, want: bytes) -> None:
+    if len(want) != 32:
+        raise ValueError("a digest is 32 bytes")
+    _ok(lib.iso_contract_check(ctypes.byref(c), want), "iso_contract_check")
+
+
+def check_partitions(c: Contract, partitions: int) -> None:
+    _ok(lib.iso_check_partitions(ctypes.byref(c), partitions), "iso_check_partitions")
+
+
+# ---------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bf16_ptr(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 (bfloat16 or 16-bit integer bit patterns)")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _dev_ptr(t, name, dtype):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError(f"{name} must be a torch tensor of {dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes, device, ws):
+    torch = _torch()
+    if nbytes == 0:
+        return ws, (0 if ws is None else ws.numel() * ws.element_size())
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def gemm_workspace(c: Contract, M: int, N: int, partitions: int = 1) -> int:
+    n = lib.iso_gemm_workspace(ctypes.byref(c), M, N, partitions)
+    if n == _BAD_SIZE:
+        raise IsoError(1, "iso_gemm_workspace")
+    return n
+
+
+def gemm(A, Wt, c: Contract, *, out=None, out_dtype: int = F32, partitions: int = 1,
+         workspace=None, stream=None):
+    """C = A @ Wt.T with the contract's leaves and tree.  Returns C."""
+    torch = _torch()
+    M, K = A.shape
+    N = Wt.shape[0]
+    if Wt.dim() != 2 or Wt.shape[1] != K:
+        raise ValueError("Wt must be [N][K]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if out_dtype == F32 else torch.bfloat16,
+                          device=A.device)
+    optr = _dev_ptr(out, "out", torch.float32 if out_dtype == F32 else out.dtype)
+    if out_dtype == BF16 and out.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("bf16 output tensor expected")
+    if out.shape != (M, N):
+        raise ValueError("out must be [M][N]")
+    need = gemm_workspace(c, M, N, partitions)
+    ws, wsb = _workspace(need, A.device, workspace)
+    _ok(lib.iso_gemm(ctypes.byref(c), _bf16_ptr(A, "A"), _bf16_ptr(Wt, "Wt"), optr, out_dtype,
+                     M, N, K, partitions, None if ws is None else ws.data_ptr(), wsb,
+                     _stream(stream)), "iso_gemm")
+    return out
+
+
+def gemm_baseline(A, Wt, *, out=None, out_dtype: int = F32, stream=None):
+    """Non-invariant comparison GEMM (one accumulator over all of K)."""
+    torch = _torch()
+    M, K = A.shape
+    N = Wt.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if out_dtype == F32 else torch.bfloat16,
+                          device=A.device)
+    _ok(lib.iso_gemm_baseline(_bf16_ptr(A, "A"), _bf16_ptr(Wt, "Wt"), out.data_ptr(), out_dtype,
+                              M, N, K, _stream(stream)), "iso_gemm_baseline")
+    return out
+
+
+def lmhead_workspace(c: Contract, M: int, V: int, partitions: int = 1) -> int:
+    n = lib.iso_lmhead_workspace(ctypes.byref(c), M, V, partitions)
+    if n == _BAD_SIZE:
+        raise IsoError(1, "iso_lmhead_workspace")
+    return n
+
+
+def lmhead_logprob(H, Wvt, tok, c: Contract, *, out=None, partitions: int = 1,
+                   workspace=None, stream=None):
+    """logprob[i] = log softmax(H[i] @ Wvt.T)[tok[i]] (FP32)."""
+    torch = _torch()
+    M, K = H.shape
+    V = Wvt.shape[0]
+    if Wvt.dim() != 2 or Wvt.shape[1] != K:
+        raise ValueError("Wvt must be [V][K]")
+    if tok.shape != (M,):
+        raise ValueError("tok must be [M]")
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=H.device)
+    need = lmhead_workspace(c, M, V, partitions)
+    ws, wsb = _workspace(need, H.device, workspace)
+    _ok(lib.iso_lmhead_logprob(ctypes.byref(c), _bf16_ptr(H, "H"), _bf16_ptr(Wvt, "Wvt"),
+                               _dev_ptr(tok, "tok", torch.int32),
+                               _dev_ptr(out, "out", torch.float32), M, V, K, partitions,
+                               None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
+        "iso_lmhead_logprob")
+    return out

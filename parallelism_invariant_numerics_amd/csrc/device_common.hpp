@@ -1,0 +1,71 @@
+// device_common.hpp -- shared device helpers for the gfx950 kernels.
+//
+// Every kernel that produces or consumes the invariant numbers uses these
+// single definitions (bf16 rounding, exp/log, the fixed-tree folds), compiled
+// with the same flags (no fast-math, no FP contraction), so the same inputs
+// give the same bits in every kernel that calls them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iso {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bit pattern, round to nearest, ties to even (finite inputs;
+// NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u)
+        return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// e^x for x <= 0 as 2^(x * log2 e) on the hardware exp2 (one rounding of the
+// product, then v_exp_f32).  Used for every softmax term in the library.
+__device__ __forceinline__ float exp_neg(float x)
+{
+    const float kLog2e = 1.44269504088896340736f;
+    return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// Natural log for the final logprob (one call per row): ROCm's logf.
+__device__ __forceinline__ float log_f32(float x) { return logf(x); }
+
+// The softmax chunk merge (m, s) + (m', s') = (u, s e^(m-u) + s' e^(m'-u)),
+// u = max(m, m').  Commutative bit for bit; (-inf, 0) is its identity, and
+// two identities give the identity (never exp(-inf - -inf)).
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2)
+{
+    float u = fmaxf(m, m2);
+    if (u == -INFINITY) {
+        m = -INFINITY;
+        s = 0.0f;
+        return;
+    }
+    float a = s * exp_neg(m - u);
+    float b = s2 * exp_neg(m2 - u);
+    m = u;
+    s = a + b;
+}
+
+// Butterfly exchange within a wave (lane ^ mask), via ds_swizzle/bpermute.
+__device__ __forceinline__ float shfl_xor(float v, int mask)
+{
+    return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace iso

@@ -1,0 +1,155 @@
+// gemm.hip -- invariant GEMM, partition combine and the non-invariant
+// comparison GEMM for gfx950.
+//
+// "IsoExec: Eliminating Trainer-Inference Mismatch in SkyRL" (agentlenshq),
+// section "Achieving Parallelism Invariance", TP bullet: contiguous K leaves,
+// FP32 accumulation, a fixed rank-to-leaf map and a fixed binary tree.  A
+// partition ("emulated rank") p of P owns leaves [p L/P, (p+1) L/P); its
+// workgroups write that subtree's root, and the combine kernel applies the
+// top log2(P) levels of the same tree, so every P gives the same bits.
+#include "gemm_core.hpp"
+#include "kernels.h"
+
+namespace iso {
+
+enum OutMode : int { kOutF32 = 0, kOutBF16 = 1, kOutWorkspace = 2 };
+
+struct GemmParams {
+    const uint16_t *A;
+    const uint16_t *Wt;
+    void *out;
+    int64_t M, N, K;
+    int64_t k_per_part;   // K columns owned by one partition
+    int stages_per_leaf;  // leaf_size / 64
+    int mode;             // OutMode
+};
+
+// Build the per-thread staging pointers of a dense tile.  Rows or columns
+// past the matrix edge are clamped to the last valid one: their products land
+// only in outputs that are never stored, and MFMA keeps outputs independent.
+__device__ __forceinline__ TileSrc dense_src(const uint16_t *A, const uint16_t *Wt, int64_t M,
+                                             int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                             int64_t k0)
+{
+    TileSrc s;
+    const int tid = threadIdx.x;
+    const int64_t kc = k0 + (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int64_t r = m0 + (tid >> 3) + 32 * i;
+        r = r < M ? r : M - 1;
+        s.a[i] = A + r * K + kc;
+        int64_t c = n0 + (tid >> 3) + 32 * i;
+        c = c < N ? c : N - 1;
+        s.b[i] = Wt + c * K + kc;
+    }
+    return s;
+}
+
+template <int LOG>
+__global__ __launch_bounds__(kThreads) void gemm_leaf_kernel(GemmParams p)
+{
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
+    const int part = blockIdx.z;
+
+    TileSrc src = dense_src(p.A, p.Wt, p.M, p.N, p.K, m0, n0, part * p.k_per_part);
+    Acc root;
+    leaf_tree_mainloop<LOG>(src, p.stages_per_leaf, lds, root);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + tile_row(lane, wr, i, r);
+                const int64_t col = n0 + tile_col(lane, wc, j);
+                if (row >= p.M || col >= p.N)
+                    continue;
+                const float v = root.v[i][j][r];
+                if (p.mode == kOutF32) {
+                    static_cast<float *>(p.out)[row * p.N + col] = v;
+                } else if (p.mode == kOutBF16) {
+                    static_cast<uint16_t *>(p.out)[row * p.N + col] = f32_to_bf16_rne(v);
+                } else {
+                    static_cast<float *>(p.out)[(static_cast<int64_t>(part) * p.M + row) * p.N +
+                                                col] = v;
+                }
+            }
+}
+
+// Top log2(P) tree levels over the partition roots ws[p][M][N].
+template <int P>
+__global__ __launch_bounds__(256) void partition_combine_kernel(const float *ws, void *out,
+                                                                int64_t MN, int out_bf16)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < MN;
+         e += stride) {
+        float r[P];
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+            r[q] = ws[q * MN + e];
+        const float v = fold_roots<P>(r);
+        if (out_bf16)
+            static_cast<uint16_t *>(out)[e] = f32_to_bf16_rne(v);
+        else
+            static_cast<float *>(out)[e] = v;
+    }
+}
+
+template <int LOG>
+static hipError_t launch_leaf(const GemmParams &p, int parts, hipStream_t stream)
+{
+    dim3 grid(static_cast<unsigned>((p.N + BN - 1) / BN), static_cast<unsigned>((p.M + BM - 1) / BM),
+              static_cast<unsigned>(parts));
+    hipLaunchKernelGGL(gemm_leaf_kernel<LOG>, grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_partials(const uint16_t *A, const uint16_t *Wt, void *out, int mode,
+                                int64_t M, int64_t N, int64_t K, int leaves_per_part,
+                                int leaf_size, int parts, hipStream_t stream)
+{
+    GemmParams p;
+    p.A = A;
+    p.Wt = Wt;
+    p.out = out;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.k_per_part = static_cast<int64_t>(leaves_per_part) * leaf_size;
+    p.stages_per_leaf = leaf_size / BK;
+    p.mode = mode;
+    switch (leaves_per_part) {
+    case 1: return launch_leaf<0>(p, parts, stream);
+    case 2: return launch_leaf<1>(p, parts, stream);
+    case 4: return launch_leaf<2>(p, parts, stream);
+    case 8: return launch_leaf<3>(p, parts, stream);
+    case 16: return launch_leaf<4>(p, parts, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_partition_combine(const float *ws, void *out, int out_bf16, int64_t MN, int parts,
+                                    hipStream_t stream)
+{
+    int64_t blocks = (MN + 255) / 256;
+    if (blocks > 8192)
+        blocks = 8192;
+    dim3 grid(static_cast<unsigned>(blocks));
+    switch (parts) {
+    case 2: hipLaunchKernelGGL(partition_combine_kernel<2>, grid, dim3(256), 0, stream, ws, out, MN, out_bf16); break;
+    case 4: hipLaunchKernelGGL(partition_combine_kernel<4>, grid, dim3(256), 0, stream, ws, out, MN, out_bf16); break;
+    case 8: hipLaunchKernelGGL(partition_combine_kernel<8>, grid, dim3(256), 0, stream, ws, out, MN, out_bf16); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace iso

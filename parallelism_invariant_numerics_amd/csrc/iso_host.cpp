@@ -1,0 +1,294 @@
+// iso_host.cpp -- the C ABI: contract validation and identity, topology
+// claims, workspace sizing and kernel dispatch.  Every check runs before the
+// first HIP call of an entry point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/iso.h"
+#include "kernels.h"
+#include "sha256.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;   // LM-head rows, T * top_k
+constexpr int64_t kMaxDim = (int64_t)1 << 23;    // GEMM M and N (tile grid limits)
+constexpr int64_t kMaxK = (int64_t)1 << 22;
+constexpr int64_t kMaxVocab = (int64_t)1 << 20;  // the chunk tree's per-row fold width
+constexpr int kMaxLeavesPerTile = 16;           // the kernels' register tree depth
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Contract validity for a region; chunk = the vocab_chunk the region needs.
+iso_status check_contract(const iso_contract *c, uint32_t chunk)
+{
+    iso_status s = iso_contract_validate(c);
+    if (s != ISO_OK)
+        return s;
+    if (c->vocab_chunk != chunk)
+        return ISO_ERR_CONTRACT;
+    return ISO_OK;
+}
+
+// Internal partition count: the caller's P, raised when a partition's leaf
+// block is deeper than the register tree holds.  Raising it only moves tree
+// levels from registers to the combine step; the tree is the same.
+int internal_parts(const iso_contract *c, int partitions)
+{
+    int lpp = (int)c->leaf_count / partitions;
+    return lpp > kMaxLeavesPerTile ? (int)c->leaf_count / kMaxLeavesPerTile : partitions;
+}
+
+iso_status launch_status(hipError_t e) { return e == hipSuccess ? ISO_OK : ISO_ERR_LAUNCH; }
+
+struct LmLayout {
+    size_t stats, target, roots, total;
+};
+
+LmLayout lm_layout(int64_t M, int64_t V, int parts)
+{
+    const int64_t nchunk = (V + ISO_VOCAB_CHUNK - 1) / ISO_VOCAB_CHUNK;
+    LmLayout l;
+    l.stats = 0;
+    l.target = align_up((size_t)M * (size_t)nchunk * 2 * sizeof(float));
+    l.roots = l.target + align_up((size_t)M * sizeof(float));
+    l.total = l.roots + (parts > 1 ? align_up((size_t)parts * M * V * sizeof(float)) : 0);
+    return l;
+}
+
+iso_status check_gemm_shape(const iso_contract *c, int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ISO_ERR_ARG;
+    if (K != (int64_t)c->leaf_count * c->leaf_size)
+        return ISO_ERR_SHAPE;
+    if (M >= kMaxRows || N >= kMaxRows || K > kMaxK)
+        return ISO_ERR_SHAPE;
+    return ISO_OK;
+}
+
+iso_status check_gemm_dims(int64_t M, int64_t N)
+{
+    return (M >= kMaxDim || N >= kMaxDim) ? ISO_ERR_SHAPE : ISO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+iso_status iso_contract_init(iso_contract *c, uint32_t leaf_count, uint32_t leaf_size,
+                             uint32_t vocab_chunk)
+{
+    if (!c)
+        return ISO_ERR_ARG;
+    c->abi_version = ISO_ABI_VERSION;
+    c->in_dtype = ISO_BF16;
+    c->accum_dtype = ISO_F32;
+    c->leaf_count = leaf_count;
+    c->leaf_size = leaf_size;
+    c->tree = ISO_TREE_BALANCED;
+    c->vocab_chunk = vocab_chunk;
+    c->schedule = ISO_SCHED_MFMA16X16X32_KASC;
+    return ISO_OK;
+}
+
+iso_status iso_contract_validate(const iso_contract *c)
+{
+    if (!c)
+        return ISO_ERR_ARG;
+    if (c->abi_version != ISO_ABI_VERSION)
+        return ISO_ERR_CONTRACT;
+    if (c->in_dtype != ISO_BF16 || c->accum_dtype != ISO_F32)
+        return ISO_ERR_DTYPE;
+    if (!is_pow2(c->leaf_count) || c->leaf_count > 64)
+        return ISO_ERR_CONTRACT;
+    if (c->leaf_size < 64 || c->leaf_size > 65536 || c->leaf_size % 64 != 0)
+        return ISO_ERR_CONTRACT;
+    if (c->tree != ISO_TREE_BALANCED || c->schedule != ISO_SCHED_MFMA16X16X32_KASC)
+        return ISO_ERR_CONTRACT;
+    if (c->vocab_chunk != 0 && c->vocab_chunk != ISO_VOCAB_CHUNK)
+        return ISO_ERR_CONTRACT;
+    return ISO_OK;
+}
+
+iso_status iso_contract_digest(const iso_contract *c, uint8_t out[32])
+{
+    if (!out)
+        return ISO_ERR_ARG;
+    iso_status s = iso_contract_validate(c);
+    if (s != ISO_OK)
+        return s;
+    static const char kTag[] = "iso.numerical_policy.v1";  // 23 chars + NUL
+    static_assert(sizeof(kTag) == 24, "tag is 24 bytes with its NUL");
+    uint8_t msg[24 + 32];
+    memcpy(msg, kTag, 24);
+    const uint32_t f[8] = {c->abi_version, c->in_dtype, c->accum_dtype, c->leaf_count,
+                           c->leaf_size, c->tree, c->vocab_chunk, c->schedule};
+    for (int i = 0; i < 8; ++i)
+        for (int b = 0; b < 4; ++b)
+            msg[24 + 4 * i + b] = (uint8_t)(f[i] >> (8 * b));
+    iso::sha256(msg, sizeof msg, out);
+    return ISO_OK;
+}
+
+iso_status iso_contract_check(const iso_contract *c, const uint8_t want[32])
+{
+    if (!want)
+        return ISO_ERR_ARG;
+    uint8_t got[32];
+    iso_status s = iso_contract_digest(c, got);
+    if (s != ISO_OK)
+        return s;
+    return memcmp(got, want, 32) == 0 ? ISO_OK : ISO_ERR_IDENTITY;
+}
+
+iso_status iso_check_partitions(const iso_contract *c, int partitions)
+{
+    iso_status s = iso_contract_validate(c);
+    if (s != ISO_OK)
+        return s;
+    if (partitions != 1 && partitions != 2 && partitions != 4 && partitions != 8)
+        return ISO_ERR_CLAIM;
+    if ((int)c->leaf_count % partitions != 0)
+        return ISO_ERR_CLAIM;
+    return ISO_OK;
+}
+
+size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int partitions)
+{
+    if (check_contract(c, 0) != ISO_OK || iso_check_partitions(c, partitions) != ISO_OK)
+        return (size_t)-1;
+    if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim)
+        return (size_t)-1;
+    int parts = internal_parts(c, partitions);
+    return parts > 1 ? (size_t)parts * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *C,
+                    uint32_t out_dtype, int64_t M, int64_t N, int64_t K, int partitions,
+                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    iso_status s = check_contract(c, 0);
+    if (s != ISO_OK)
+        return s;
+    if ((s = check_gemm_shape(c, M, N, K)) != ISO_OK)
+        return s;
+    if ((s = check_gemm_dims(M, N)) != ISO_OK)
+        return s;
+    if (out_dtype != ISO_F32 && out_dtype != ISO_BF16)
+        return ISO_ERR_DTYPE;
+    if ((s = iso_check_partitions(c, partitions)) != ISO_OK)
+        return s;
+    if (M == 0 || N == 0)
+        return ISO_OK;
+    if (!A || !Wt || !C || !aligned16(A) || !aligned16(Wt))
+        return ISO_ERR_ARG;
+    const int parts = internal_parts(c, partitions);
+    const size_t need = iso_gemm_workspace(c, M, N, partitions);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return ISO_ERR_WORKSPACE;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int lpp = (int)c->leaf_count / parts;
+    const int bf16 = out_dtype == ISO_BF16;
+    if (parts == 1)
+        return launch_status(iso::launch_gemm_partials(
+            static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Wt), C, bf16 ? 1 : 0,
+            M, N, K, lpp, (int)c->leaf_size, 1, st));
+    hipError_t e = iso::launch_gemm_partials(static_cast<const uint16_t *>(A),
+                                             static_cast<const uint16_t *>(Wt), workspace, 2, M,
+                                             N, K, lpp, (int)c->leaf_size, parts, st);
+    if (e != hipSuccess)
+        return ISO_ERR_LAUNCH;
+    return launch_status(iso::launch_partition_combine(static_cast<const float *>(workspace), C,
+                                                       bf16, M * N, parts, st));
+}
+
+iso_status iso_gemm_baseline(const void *A, const void *Wt, void *C, uint32_t out_dtype,
+                             int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ISO_ERR_ARG;
+    if (K == 0 || K % 64 != 0 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
+        return ISO_ERR_SHAPE;
+    if (out_dtype != ISO_F32 && out_dtype != ISO_BF16)
+        return ISO_ERR_DTYPE;
+    if (M == 0 || N == 0)
+        return ISO_OK;
+    if (!A || !Wt || !C || !aligned16(A) || !aligned16(Wt))
+        return ISO_ERR_ARG;
+    // one leaf spanning all of K: a single accumulator, no tree
+    return launch_status(iso::launch_gemm_partials(
+        static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Wt), C,
+        out_dtype == ISO_BF16 ? 1 : 0, M, N, K, 1, (int)K, 1, static_cast<hipStream_t>(stream)));
+}
+
+size_t iso_lmhead_workspace(const iso_contract *c, int64_t M, int64_t V, int partitions)
+{
+    if (check_contract(c, ISO_VOCAB_CHUNK) != ISO_OK ||
+        iso_check_partitions(c, partitions) != ISO_OK)
+        return (size_t)-1;
+    if (M < 0 || V < 1 || M >= kMaxRows || V > kMaxVocab)
+        return (size_t)-1;
+    return lm_layout(M, V, internal_parts(c, partitions)).total;
+}
+
+iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *Wvt,
+                              const int32_t *tok, float *logprob, int64_t M, int64_t V,
+                              int64_t K, int partitions, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    iso_status s = check_contract(c, ISO_VOCAB_CHUNK);
+    if (s != ISO_OK)
+        return s;
+    if ((s = check_gemm_shape(c, M, V, K)) != ISO_OK)
+        return s;
+    if (V < 1 || V > kMaxVocab)
+        return ISO_ERR_SHAPE;
+    if ((s = iso_check_partitions(c, partitions)) != ISO_OK)
+        return s;
+    if (M == 0)
+        return ISO_OK;
+    if (!H || !Wvt || !tok || !logprob || !aligned16(H) || !aligned16(Wvt))
+        return ISO_ERR_ARG;
+    const int parts = internal_parts(c, partitions);
+    const LmLayout l = lm_layout(M, V, parts);
+    if (!workspace || workspace_bytes < l.total || !aligned16(workspace))
+        return ISO_ERR_WORKSPACE;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    float *stats = reinterpret_cast<float *>(ws + l.stats);
+    float *target = reinterpret_cast<float *>(ws + l.target);
+    float *roots = parts > 1 ? reinterpret_cast<float *>(ws + l.roots) : nullptr;
+    hipError_t e = iso::launch_lmhead_stats(
+        static_cast<const uint16_t *>(H), static_cast<const uint16_t *>(Wvt), tok, stats, target,
+        roots, M, V, K, (int)c->leaf_count / parts, (int)c->leaf_size, parts, st);
+    if (e != hipSuccess)
+        return ISO_ERR_LAUNCH;
+    return launch_status(iso::launch_lmhead_finish(stats, target, tok, logprob, M, V, st));
+}
+
+const char *iso_status_str(iso_status s)
+{
+    switch (s) {
+    case ISO_OK: return "ok";
+    case ISO_ERR_ARG: return "invalid argument";
+    case ISO_ERR_SHAPE: return "shape does not fit the contract or the size limits";
+    case ISO_ERR_DTYPE: return "unsupported dtype";
+    case ISO_ERR_CLAIM: return "partition count outside the contract's topology claim";
+    case ISO_ERR_IDENTITY: return "contract digest differs from the expected identity";
+    case ISO_ERR_WORKSPACE: return "workspace missing or too small";
+    case ISO_ERR_LAUNCH: return "kernel launch failed";
+    case ISO_ERR_CONTRACT: return "malformed contract";
+    }
+    return "unknown status";
+}
+
+const char *iso_version(void) { return "iso 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public interface is include/iso.h).  Each launcher only
+// enqueues work on `stream` and returns hipGetLastError() of its launches.
+// Arguments are validated by the caller (iso_host.cpp) before any launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iso {
+
+// Leaf/tree GEMM over `parts` contiguous leaf blocks of `leaves_per_part`
+// leaves (1..16) each.  mode 0: FP32 C [M][N]; 1: bf16 C; 2: FP32 partition
+// roots ws[parts][M][N].
+hipError_t launch_gemm_partials(const uint16_t *A, const uint16_t *Wt, void *out, int mode,
+                                int64_t M, int64_t N, int64_t K, int leaves_per_part,
+                                int leaf_size, int parts, hipStream_t stream);
+
+// out[e] = fixed tree over ws[0..parts)[e], e < MN; FP32 or bf16 output.
+hipError_t launch_partition_combine(const float *ws, void *out, int out_bf16, int64_t MN,
+                                    int parts, hipStream_t stream);
+
+// LM-head: chunk statistics ws_stats [M][nchunk] (float2: chunk max, chunk
+// exp-sum) and the target logit ws_target [M].  parts == 1 fuses the stats
+// into the leaf/tree main loop; parts > 1 first writes partition roots of the
+// logits to ws_roots [parts][M][V].
+hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int32_t *tok,
+                               float *ws_stats, float *ws_target, float *ws_roots, int64_t M,
+                               int64_t V, int64_t K, int leaves_per_part, int leaf_size,
+                               int parts, hipStream_t stream);
+
+// Per row: fixed tree over the chunk statistics, then the logprob.
+hipError_t launch_lmhead_finish(const float *ws_stats, const float *ws_target,
+                                const int32_t *tok, float *logprob, int64_t M, int64_t V,
+                                hipStream_t stream);
+
+struct MoeBuffers {
+    int32_t *idx;       // [T][k]
+    float *gate;        // [T][k]
+    uint16_t *h;        // [T][k][I]
+    float *e;           // [T][k][H]
+    int32_t *counts;    // [E]
+    int32_t *offsets;   // [E + 1]
+    int32_t *rows;      // [T * k] (token * k + slot), grouped by expert, token order
+    int32_t *tiles;     // [max_tiles][2]: (expert, first row within the expert)
+    int32_t *ntiles;    // [1]
+    int max_tiles;
+};
+
+hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg,
+                      const uint16_t *Wu, const uint16_t *Wd, float *Y, int64_t T, int64_t H,
+                      int64_t E, int64_t I, int top_k, int gu_leaves, int gu_leaf_size,
+                      int dn_leaves, int dn_leaf_size, const MoeBuffers &b, hipStream_t stream);
+
+}  // namespace iso

@@ -1,0 +1,331 @@
+// lmhead.hip -- fused LM-head log-softmax statistics and sampled-token
+// logprob for gfx950.
+//
+// The rollout engine records the sampled token's logprob and the trainer
+// recomputes it (katelyatop-blog post on vLLM/SkyRL IsoExec, section 1 and
+// section 4); both must see the same bits, so the softmax reduction is a
+// fixed tree too ("IsoExec: Eliminating Trainer-Inference Mismatch in SkyRL",
+// section "Achieving Parallelism Invariance": partials are combined by a
+// fixed binary tree regardless of layout).
+//
+// Tree over the vocabulary:
+//   chunk = 128 consecutive token ids = one workgroup tile's columns;
+//   chunk max: exact (order-free);
+//   chunk sum of exp(z - chunk max): balanced binary tree over the 128 ids in
+//     index order -- lanes (l, l^1), (l, l^2), (l, l^4), (l, l^8) hold
+//     neighbouring columns of a 16-wide MFMA block, then the four blocks of a
+//     wave pair up in registers, then the two waves through LDS;
+//   chunk merge: balanced binary tree over chunk index with the (m, s) merge
+//     of device_common.hpp, padded with (-inf, 0).
+// The logits never leave registers on the fused path (one partition).  With
+// several partitions the partition roots of the logits go through the
+// workspace and the same epilogue function runs on their folded values.
+#include "gemm_core.hpp"
+#include "kernels.h"
+
+namespace iso {
+
+constexpr int kChunk = BN;  // 128 token ids per chunk = one tile's columns
+
+struct LmArgs {
+    const uint16_t *H;
+    const uint16_t *Wvt;
+    const int32_t *tok;
+    float *stats;   // [M][nchunk][2]
+    float *target;  // [M]
+    const float *roots;  // [parts][M][V] (several partitions only)
+    int64_t M, V, K, nchunk;
+    int stages_per_leaf;
+};
+
+// Chunk statistics of one 128 x 128 logit tile held in MFMA layout.
+// `red` is LDS scratch of at least 512 floats, free for use on entry.
+__device__ __forceinline__ void chunk_stats_epilogue(const Acc &z, int64_t m0, int64_t n0,
+                                                     const LmArgs &a, float *red)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int64_t chunk = n0 / kChunk;
+
+    bool colv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        colv[j] = n0 + tile_col(lane, wc, j) < a.V;
+
+    // half-chunk (64 columns) maxima per row, then the chunk maximum
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (colv[j])
+                    m = fmaxf(m, z.v[i][j][r]);
+            m = fmaxf(m, shfl_xor(m, 1));
+            m = fmaxf(m, shfl_xor(m, 2));
+            m = fmaxf(m, shfl_xor(m, 4));
+            m = fmaxf(m, shfl_xor(m, 8));
+            if ((lane & 15) == 0)
+                red[wc * 128 + tile_row(lane, wr, i, r)] = m;
+        }
+    __syncthreads();
+
+    float cm[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rt = tile_row(lane, wr, i, r);
+            cm[i][r] = fmaxf(red[rt], red[128 + rt]);
+        }
+
+    // exp-sums: 16-column blocks by lane butterfly, then blocks, then waves
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float blk[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float e = colv[j] ? exp_neg(z.v[i][j][r] - cm[i][r]) : 0.0f;
+                e = e + shfl_xor(e, 1);
+                e = e + shfl_xor(e, 2);
+                e = e + shfl_xor(e, 4);
+                e = e + shfl_xor(e, 8);
+                blk[j] = e;
+            }
+            const float half = (blk[0] + blk[1]) + (blk[2] + blk[3]);
+            if ((lane & 15) == 0)
+                red[256 + wc * 128 + tile_row(lane, wr, i, r)] = half;
+        }
+    __syncthreads();
+
+    if (wc == 0 && (lane & 15) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rt = tile_row(lane, wr, i, r);
+                const int64_t row = m0 + rt;
+                if (row < a.M) {
+                    const float s = red[256 + rt] + red[256 + 128 + rt];
+                    float *st = a.stats + (row * a.nchunk + chunk) * 2;
+                    st[0] = cm[i][r];
+                    st[1] = s;
+                }
+            }
+    }
+
+    // the sampled token's logit: written by the one lane that holds it
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + tile_row(lane, wr, i, r);
+            if (row >= a.M)
+                continue;
+            const int64_t t = a.tok[row];
+            const int64_t rel = t - n0 - wc * 64 - (lane & 15);
+            if (rel >= 0 && rel < 64 && (rel & 15) == 0 && t < a.V) {
+                const int j = static_cast<int>(rel >> 4);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (jj == j)
+                        a.target[row] = z.v[i][jj][r];
+            }
+        }
+}
+
+template <int LOG>
+__global__ __launch_bounds__(kThreads) void lmhead_fused_kernel(LmArgs a)
+{
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+
+    TileSrc src;
+    {
+        const int tid = threadIdx.x;
+        const int64_t kc = (tid & 7) * 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int64_t r = m0 + (tid >> 3) + 32 * i;
+            r = r < a.M ? r : a.M - 1;
+            src.a[i] = a.H + r * a.K + kc;
+            int64_t c = n0 + (tid >> 3) + 32 * i;
+            c = c < a.V ? c : a.V - 1;
+            src.b[i] = a.Wvt + c * a.K + kc;
+        }
+    }
+    Acc z;
+    leaf_tree_mainloop<LOG>(src, a.stages_per_leaf, lds, z);
+    chunk_stats_epilogue(z, m0, n0, a, reinterpret_cast<float *>(lds));
+}
+
+// Several partitions: fold the partition roots of the logits with the top
+// tree levels, in the MFMA layout, then the same epilogue.
+template <int P>
+__global__ __launch_bounds__(kThreads) void lmhead_roots_kernel(LmArgs a)
+{
+    __shared__ float red[512];
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int64_t MV = a.M * a.V;
+    Acc z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                int64_t row = m0 + tile_row(lane, wr, i, r);
+                int64_t col = n0 + tile_col(lane, wc, j);
+                row = row < a.M ? row : a.M - 1;
+                col = col < a.V ? col : a.V - 1;
+                float rv[P];
+#pragma unroll
+                for (int q = 0; q < P; ++q)
+                    rv[q] = a.roots[q * MV + row * a.V + col];
+                z.v[i][j][r] = fold_roots<P>(rv);
+            }
+    chunk_stats_epilogue(z, m0, n0, a, red);
+}
+
+// Per row: balanced tree over the chunk statistics in chunk order, then
+// logprob = (z_t - max) - log(sum).  One 256-thread workgroup per row;
+// thread t folds chunks [t*PER, (t+1)*PER), then lanes and waves pair up.
+template <int PER>
+__global__ __launch_bounds__(256) void lmhead_finish_kernel(const float *stats,
+                                                            const float *target,
+                                                            const int32_t *tok, float *logprob,
+                                                            int64_t M, int64_t V, int64_t nchunk)
+{
+    __shared__ float wm[4], ws[4];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    float m[PER], s[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int64_t c = static_cast<int64_t>(tid) * PER + q;
+        if (c < nchunk) {
+            m[q] = stats[(row * nchunk + c) * 2 + 0];
+            s[q] = stats[(row * nchunk + c) * 2 + 1];
+        } else {
+            m[q] = -INFINITY;
+            s[q] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int width = PER; width > 1; width >>= 1)
+#pragma unroll
+        for (int q = 0; q < width / 2; ++q) {
+            float mm = m[2 * q], ss = s[2 * q];
+            lse_merge(mm, ss, m[2 * q + 1], s[2 * q + 1]);
+            m[q] = mm;
+            s[q] = ss;
+        }
+    float mv = m[0], sv = s[0];
+#pragma unroll
+    for (int mask = 1; mask < 64; mask <<= 1) {
+        const float m2 = shfl_xor(mv, mask);
+        const float s2 = shfl_xor(sv, mask);
+        lse_merge(mv, sv, m2, s2);
+    }
+    if ((tid & 63) == 0) {
+        wm[tid >> 6] = mv;
+        ws[tid >> 6] = sv;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float m01 = wm[0], s01 = ws[0];
+        lse_merge(m01, s01, wm[1], ws[1]);
+        float m23 = wm[2], s23 = ws[2];
+        lse_merge(m23, s23, wm[3], ws[3]);
+        lse_merge(m01, s01, m23, s23);
+        const int64_t t = tok[row];
+        float lp;
+        if (t < 0 || t >= V)
+            lp = __builtin_nanf("");
+        else
+            lp = (target[row] - m01) - log_f32(s01);
+        logprob[row] = lp;
+    }
+}
+
+template <int LOG>
+static hipError_t launch_fused(const LmArgs &a, hipStream_t stream)
+{
+    dim3 grid(static_cast<unsigned>((a.M + BM - 1) / BM), static_cast<unsigned>(a.nchunk));
+    hipLaunchKernelGGL(lmhead_fused_kernel<LOG>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int32_t *tok,
+                               float *ws_stats, float *ws_target, float *ws_roots, int64_t M,
+                               int64_t V, int64_t K, int leaves_per_part, int leaf_size,
+                               int parts, hipStream_t stream)
+{
+    LmArgs a;
+    a.H = H;
+    a.Wvt = Wvt;
+    a.tok = tok;
+    a.stats = ws_stats;
+    a.target = ws_target;
+    a.roots = ws_roots;
+    a.M = M;
+    a.V = V;
+    a.K = K;
+    a.nchunk = (V + kChunk - 1) / kChunk;
+    a.stages_per_leaf = leaf_size / BK;
+    if (parts == 1) {
+        switch (leaves_per_part) {
+        case 1: return launch_fused<0>(a, stream);
+        case 2: return launch_fused<1>(a, stream);
+        case 4: return launch_fused<2>(a, stream);
+        case 8: return launch_fused<3>(a, stream);
+        case 16: return launch_fused<4>(a, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    hipError_t e = launch_gemm_partials(H, Wvt, ws_roots, 2, M, V, K, leaves_per_part, leaf_size,
+                                        parts, stream);
+    if (e != hipSuccess)
+        return e;
+    dim3 grid(static_cast<unsigned>((M + BM - 1) / BM), static_cast<unsigned>(a.nchunk));
+    switch (parts) {
+    case 2: hipLaunchKernelGGL(lmhead_roots_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(lmhead_roots_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(lmhead_roots_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_lmhead_finish(const float *ws_stats, const float *ws_target,
+                                const int32_t *tok, float *logprob, int64_t M, int64_t V,
+                                hipStream_t stream)
+{
+    const int64_t nchunk = (V + kChunk - 1) / kChunk;
+    int64_t pad = 256;
+    while (pad < nchunk)
+        pad <<= 1;
+    const int64_t per = pad / 256;
+    dim3 grid(static_cast<unsigned>(M));
+    switch (per) {
+    case 1: hipLaunchKernelGGL(lmhead_finish_kernel<1>, grid, dim3(256), 0, stream, ws_stats, ws_target, tok, logprob, M, V, nchunk); break;
+    case 2: hipLaunchKernelGGL(lmhead_finish_kernel<2>, grid, dim3(256), 0, stream, ws_stats, ws_target, tok, logprob, M, V, nchunk); break;
+    case 4: hipLaunchKernelGGL(lmhead_finish_kernel<4>, grid, dim3(256), 0, stream, ws_stats, ws_target, tok, logprob, M, V, nchunk); break;
+    case 8: hipLaunchKernelGGL(lmhead_finish_kernel<8>, grid, dim3(256), 0, stream, ws_stats, ws_target, tok, logprob, M, V, nchunk); break;
+    case 16: hipLaunchKernelGGL(lmhead_finish_kernel<16>, grid, dim3(256), 0, stream, ws_stats, ws_target, tok, logprob, M, V, nchunk); break;
+    case 32: hipLaunchKernelGGL(lmhead_finish_kernel<32>, grid, dim3(256), 0, stream, ws_stats, ws_target, tok, logprob, M, V, nchunk); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace iso

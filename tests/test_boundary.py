@@ -1,0 +1,158 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and exports
+every declared entry point, the contract identity is SHA-256 of the documented
+canonical bytes, and every argument / shape / claim / workspace error is
+returned before any launch (fake device addresses are never dereferenced)."""
+import ctypes
+import hashlib
+import os
+import re
+import struct
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+iso = pytest.importorskip("parallelism_invariant_numerics_amd")
+
+FAKE = 0x10000  # an aligned address the host checks accept; never dereferenced
+
+
+def _declared():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(iso_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert "iso_gemm" in names and "iso_lmhead_logprob" in names
+    for n in names:
+        assert hasattr(iso.lib, n), n
+
+
+def test_version():
+    assert "gfx950" in iso.version()
+
+
+def _canonical(c):
+    return struct.pack("<24s8I", b"iso.numerical_policy.v1\0", c.abi_version, c.in_dtype,
+                       c.accum_dtype, c.leaf_count, c.leaf_size, c.tree, c.vocab_chunk,
+                       c.schedule)
+
+
+@pytest.mark.parametrize("L,m,chunk", [(4, 64, 0), (8, 256, 0), (8, 256, 128), (16, 256, 0),
+                                       (4, 512, 0), (4, 128, 0), (1, 64, 0), (64, 65536, 0)])
+def test_digest_is_sha256_of_canonical_bytes(L, m, chunk):
+    c = iso.contract(L, m, chunk)
+    assert len(_canonical(c)) == 56
+    assert iso.digest(c) == hashlib.sha256(_canonical(c)).digest()
+
+
+def test_digest_changes_with_every_field():
+    base = iso.contract(8, 256, 0)
+    d0 = iso.digest(base)
+    for L, m, chunk in [(16, 256, 0), (8, 512, 0), (8, 256, 128), (4, 256, 0)]:
+        assert iso.digest(iso.contract(L, m, chunk)) != d0
+    iso.check_identity(base, d0)
+    with pytest.raises(iso.IsoError) as e:
+        iso.check_identity(base, iso.digest(iso.contract(4, 512, 0)))
+    assert e.value.name == "ISO_ERR_IDENTITY"
+
+
+def _raw(**kw):
+    c = iso.Contract()
+    iso.lib.iso_contract_init(ctypes.byref(c), 8, 256, 0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("abi_version", 2, 8), ("in_dtype", 2, 3), ("accum_dtype", 1, 3), ("leaf_count", 3, 8),
+    ("leaf_count", 128, 8), ("leaf_count", 0, 8), ("leaf_size", 96, 8), ("leaf_size", 0, 8),
+    ("tree", 2, 8), ("schedule", 0, 8), ("vocab_chunk", 64, 8)])
+def test_malformed_contract(field, value, code):
+    c = _raw(**{field: value})
+    assert iso.lib.iso_contract_validate(ctypes.byref(c)) == code
+    out = ctypes.create_string_buffer(32)
+    assert iso.lib.iso_contract_digest(ctypes.byref(c), out) == code
+
+
+def _gemm(c, M=64, N=64, K=2048, P=1, A=FAKE, W=FAKE, C=FAKE, od=iso.F32, ws=None, wsb=0):
+    return iso.lib.iso_gemm(ctypes.byref(c), A, W, C, od, M, N, K, P, ws, wsb, None)
+
+
+def test_gemm_rejections_before_launch():
+    c = iso.contract(8, 256, 0)
+    assert _gemm(c, K=2047) == 2                      # K != L * m
+    assert _gemm(c, M=-1) == 1
+    assert _gemm(c, od=7) == 3
+    for P in (3, 16, 0, -1):
+        assert _gemm(c, P=P) == 4                      # outside the claim
+    assert _gemm(iso.contract(4, 512, 0), P=8) == 4    # P must divide L
+    assert _gemm(c, A=None) == 1
+    assert _gemm(c, W=FAKE + 2) == 1                   # 16-byte alignment
+    assert _gemm(c, P=2) == 6                          # workspace missing
+    need = iso.gemm_workspace(c, 64, 64, 2)
+    assert need == 2 * 64 * 64 * 4
+    assert _gemm(c, P=2, ws=FAKE, wsb=need - 1) == 6
+    assert _gemm(c, M=0) == 0 and _gemm(c, N=0) == 0   # empty: nothing launched
+    assert _gemm(iso.contract(8, 256, 128)) == 8       # a logprob contract on a GEMM
+    assert _gemm(c, K=1 << 23) == 2
+
+
+def test_gemm_workspace_sizes():
+    c16 = iso.contract(16, 256, 0)
+    assert iso.gemm_workspace(c16, 10, 20, 1) == 0
+    for P in (2, 4, 8):
+        assert iso.gemm_workspace(c16, 10, 20, P) == P * 10 * 20 * 4
+    # a partition deeper than the register tree is split further internally
+    assert iso.gemm_workspace(iso.contract(64, 64, 0), 10, 20, 1) == 4 * 10 * 20 * 4
+    assert iso.gemm_workspace(iso.contract(32, 64, 0), 10, 20, 1) == 2 * 10 * 20 * 4
+    with pytest.raises(iso.IsoError):
+        iso.gemm_workspace(c16, 10, 20, 3)
+
+
+def test_claims():
+    c = iso.contract(4, 64, 0)
+    for P in (1, 2, 4):
+        iso.check_partitions(c, P)
+    for P in (8, 3, 0):
+        with pytest.raises(iso.IsoError) as e:
+            iso.check_partitions(c, P)
+        assert e.value.name == "ISO_ERR_CLAIM"
+
+
+def test_baseline_rejections():
+    f = iso.lib.iso_gemm_baseline
+    assert f(FAKE, FAKE, FAKE, iso.F32, 4, 4, 100, None) == 2
+    assert f(FAKE, FAKE, FAKE, 9, 4, 4, 128, None) == 3
+    assert f(None, FAKE, FAKE, iso.F32, 4, 4, 128, None) == 1
+    assert f(FAKE, FAKE, FAKE, iso.F32, 0, 4, 128, None) == 0
+
+
+def _lm(c, M=8, V=512, K=256, P=1, ws=FAKE, wsb=1 << 40, H=FAKE, tok=FAKE):
+    return iso.lib.iso_lmhead_logprob(ctypes.byref(c), H, FAKE, tok, FAKE, M, V, K, P, ws, wsb,
+                                      None)
+
+
+def test_lmhead_rejections_before_launch():
+    c = iso.contract(4, 64, 128)
+    assert _lm(iso.contract(4, 64, 0)) == 8           # not a logprob contract
+    assert _lm(c, K=512) == 2
+    assert _lm(c, V=0) == 2
+    assert _lm(c, V=(1 << 20) + 1) == 2
+    assert _lm(c, P=8) == 4
+    assert _lm(c, H=None) == 1
+    assert _lm(c, tok=None) == 1
+    need = iso.lmhead_workspace(c, 8, 512, 1)
+    assert need > 0
+    assert _lm(c, ws=None) == 6
+    assert _lm(c, wsb=need - 1) == 6
+    assert _lm(c, M=0) == 0
+    assert iso.lmhead_workspace(c, 8, 512, 2) >= need + 2 * 8 * 512 * 4

@@ -1,0 +1,135 @@
+"""GPU parity of iso_gemm with the CPU oracle, through the C ABI.
+
+* exact cases (tree-order pins, integer inputs): bit for bit;
+* random cases: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k| per element;
+* partitions P = 1, 2, 4, 8: identical bits;
+* bf16 output: the FP32 root rounded to nearest-even, bit for bit;
+* the prefill workload at full size (4096 x 2048 x 2048, 8 leaves of 256):
+  sampled elements against the oracle, all elements across P and output dtypes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import absdot, check_gemm_tol, dev, host, note, torch, u32
+from iso_synth import f32_to_bf16_bits, make_config, normal_bf16
+from pins import tree_case_inputs, tree_pins
+
+pytestmark = pytest.mark.gpu
+
+iso = pytest.importorskip("parallelism_invariant_numerics_amd")
+
+
+def _run(A, Wt, L, P=1, out_dtype=None):
+    K = A.shape[1]
+    c = iso.contract(L, K // L, 0)
+    out = iso.gemm(dev(A), dev(Wt), c, partitions=P, out_dtype=out_dtype or iso.F32)
+    torch().cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_tree_order_pins_bitwise(P):
+    for pin in tree_pins():
+        if pin["kind"] != "tree" or pin["leaves"] % P:
+            continue
+        note(f"tree pin L={pin['leaves']} P={P}")
+        A, Wt = tree_case_inputs(pin, 64, rows=3, cols=5)
+        C = _run(A, Wt, pin["leaves"], P)
+        assert np.all(u32(C) == pin["balanced"]), hex(int(u32(C)[0, 0]))
+
+
+@pytest.mark.parametrize("M,N,K,L", [(1, 1, 64, 1), (65, 129, 256, 4), (300, 200, 2048, 8),
+                                     (128, 128, 4096, 16), (7, 300, 512, 2), (129, 17, 1024, 16)])
+def test_integer_inputs_exact(M, N, K, L):
+    note(f"integer exact M={M} N={N} K={K} L={L}")
+    rng = np.random.default_rng(M * 7 + N)
+    ai = rng.integers(-8, 9, size=(M, K))
+    wi = rng.integers(-8, 9, size=(N, K))
+    C = _run(f32_to_bf16_bits(ai.astype(np.float32)), f32_to_bf16_bits(wi.astype(np.float32)), L)
+    assert np.array_equal(C.astype(np.int64), ai @ wi.T)
+
+
+def test_tiny_workload_parity():
+    cfg = make_config("tiny")
+    note("tiny workload 8x256x512, 4 leaves of 64")
+    C = _run(cfg["A"], cfg["Wt"], cfg["leaves"])
+    ref = oracle.gemm(cfg["A"], cfg["Wt"], cfg["leaves"])
+    check_gemm_tol(C, ref, absdot(cfg["A"], cfg["Wt"]), "tiny")
+
+
+@pytest.mark.parametrize("M,N,K,L", [(257, 383, 1024, 8), (33, 640, 512, 2), (1, 130, 2048, 8),
+                                     (130, 1, 256, 4), (200, 300, 4096, 16), (64, 64, 2048, 32),
+                                     (40, 72, 4096, 64)])
+def test_random_ragged_parity(M, N, K, L):
+    note(f"random ragged M={M} N={N} K={K} L={L}")
+    A = normal_bf16(M + 1, (M, K), 1.0)
+    Wt = normal_bf16(N + 2, (N, K), 0.02)
+    C = _run(A, Wt, L)
+    check_gemm_tol(C, oracle.gemm(A, Wt, L), absdot(A, Wt), f"{M}x{N}x{K}/L{L}")
+
+
+@pytest.mark.parametrize("L", [8, 16])
+def test_partitions_bitwise(L):
+    M, N, K = 200, 300, 256 * L
+    A = normal_bf16(5, (M, K), 1.0)
+    Wt = normal_bf16(6, (N, K), 0.02)
+    note(f"partitions L={L}")
+    base = u32(_run(A, Wt, L, 1))
+    for P in (2, 4, 8):
+        assert np.array_equal(u32(_run(A, Wt, L, P)), base), P
+    bf = _run(A, Wt, L, 1, iso.BF16)
+    assert np.array_equal(bf, f32_to_bf16_bits(base.view(np.float32)))
+
+
+def test_run_to_run_determinism():
+    A = normal_bf16(7, (513, 2048), 1.0)
+    Wt = normal_bf16(8, (257, 2048), 0.02)
+    note("determinism x3")
+    runs = [u32(_run(A, Wt, 8)) for _ in range(3)]
+    assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
+
+
+def test_empty_problem():
+    c = iso.contract(4, 64, 0)
+    t = torch()
+    A = t.empty((0, 256), dtype=t.bfloat16, device="cuda")
+    Wt = t.zeros((8, 256), dtype=t.bfloat16, device="cuda")
+    out = iso.gemm(A, Wt, c)
+    assert out.shape == (0, 8)
+
+
+def test_prefill_full_size():
+    cfg = make_config("prefill")
+    A, Wt, L = cfg["A"], cfg["Wt"], cfg["leaves"]
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    c = iso.contract(L, K // L, 0)
+    t = torch()
+    dA, dW = dev(A), dev(Wt)
+    note("prefill full size P=1 fp32")
+    base = iso.gemm(dA, dW, c)
+    t.cuda.synchronize()
+    C = host(base)
+    rng = np.random.default_rng(2024)
+    rows = np.concatenate([[0, 0, M - 1, M - 1, 127, 128], rng.integers(0, M, 1500)])
+    cols = np.concatenate([[0, N - 1, 0, N - 1, 127, 128], rng.integers(0, N, 1500)])
+    ref = oracle.gemm_elems(A, Wt, L, rows, cols)
+    check_gemm_tol(C[rows, cols], ref, absdot(A, Wt, rows, cols), "prefill sampled")
+    for P in (2, 4, 8):
+        note(f"prefill full size P={P}")
+        out = iso.gemm(dA, dW, c, partitions=P)
+        t.cuda.synchronize()
+        assert np.array_equal(u32(host(out)), u32(C)), P
+    note("prefill full size bf16 out")
+    bf = host(iso.gemm(dA, dW, c, out_dtype=iso.BF16))
+    assert np.array_equal(bf, f32_to_bf16_bits(C))
+
+
+def test_baseline_accuracy():
+    M, N, K = 129, 257, 2048
+    A = normal_bf16(9, (M, K), 1.0)
+    Wt = normal_bf16(10, (N, K), 0.02)
+    note("baseline accuracy")
+    out = iso.gemm_baseline(dev(A), dev(Wt))
+    torch().cuda.synchronize()
+    check_gemm_tol(host(out), oracle.gemm(A, Wt, 8), absdot(A, Wt), "baseline")
