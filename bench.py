@@ -1,0 +1,260 @@
+"""Benchmark of the invariant matmul / token-logprob path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+One step is one invariant GEMM of the prefill-shaped linear layer
+(A [4096 x 2048] bf16 times W [2048 x 2048] bf16, 8 contiguous leaves of 256
+along K, FP32 accumulation and fixed tree, bf16 output) with its inputs
+resident in HBM; ``value`` is TFLOP/s (2 M N K per step).  The same run also
+times, as sub-measurements reported in the JSON line: the non-invariant
+comparison kernel and torch.matmul on the same shape, the invariance-sweep
+shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8 partitions, and the LM-head
+logprob workload (8192 rows x 2048 x 151936 vocabulary) in rows/s, plus a
+bitwise invariance check.  Prints ONE JSON line.
+
+Inputs are seeded synthetic data with the workloads' shapes and
+distributions (no dataset or trained weights are involved).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--quick", action="store_true", help="headline GEMM only (for profiling)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run one 1 GiB device copy first (HBM counter calibration)")
+    return p.parse_args()
+
+
+def _dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def _time_events(fn, steps, stream):
+    """Average duration (ms) of fn() measured with HIP events on `stream`."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+
+def _source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+GEMM_SOURCES = ["parallelism_invariant_numerics_amd/csrc/gemm_core.hpp",
+                "parallelism_invariant_numerics_amd/csrc/gemm.hip",
+                "parallelism_invariant_numerics_amd/csrc/device_common.hpp"]
+
+
+def _traffic(kernel_hash):
+    """Measured HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemm_leaf_prefill_hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _cpu_baseline(cfg, target_s=12.0):
+    """The oracle (untuned) on a bounded row sample of the same GEMM."""
+    import oracle
+    A, Wt, L = cfg["A"], cfg["Wt"], cfg["leaves"]
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.gemm(A[:rows], Wt, L)
+    dt = time.perf_counter() - t0
+    rows = int(min(cfg["M"], max(16, rows * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm(A[:rows], Wt, L)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * cfg["N"] * cfg["K"]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of {cfg['M']} rows of the prefill GEMM ({rows}x{cfg['N']}x{cfg['K']}, "
+                      f"8 leaves), {dt:.1f} s"}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import parallelism_invariant_numerics_amd as iso
+    from iso_synth import make_config, normal_bf16
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------- headline: prefill linear layer, invariant GEMM
+    cfg = make_config("prefill")
+    M, N, K, L = cfg["M"], cfg["N"], cfg["K"], cfg["leaves"]
+    A, W = _dev(cfg["A"]), _dev(cfg["Wt"])
+    c = iso.contract(L, K // L, 0)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    step = lambda: iso.gemm(A, W, c, out=out, out_dtype=iso.BF16)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    flop = 2.0 * M * N * K
+    value = flop * args.steps / wall / 1e12
+    kern_ms = _time_events(step, args.steps, stream)
+    achieved = flop / (kern_ms * 1e-3) / 1e12
+    src_hash = _source_hash(GEMM_SOURCES)
+    line = {
+        "metric": "invariant bf16 GEMM TFLOP/s + % MFMA peak; LM-head logprob rows/s; bitwise pass",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill linear layer: A[4096x2048] bf16 ~N(0,1) x W[2048x2048] "
+                               "bf16 ~N(0,0.02), 8 leaves of 256, FP32 accumulation, bf16 out",
+                   "M": M, "N": N, "K": K, "leaves": L, "leaf_size": K // L, "partitions": 1},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(src_hash), "kernel": "gemm_leaf_kernel<3>",
+                     "kernel_ms": round(kern_ms, 5), "algorithmic_flop": flop,
+                     "source_hash": src_hash},
+    }
+    extra = {}
+
+    # ---------------- cost of invariance on the same shape
+    outb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    base = lambda: iso.gemm_baseline(A, W, out=outb, out_dtype=iso.BF16)
+    for _ in range(3):
+        base()
+    b_ms = _time_events(base, args.steps, stream)
+    # torch's linear layer on the same [N][K] weight storage (hipBLASLt)
+    tm = lambda: torch.nn.functional.linear(A, W)
+    for _ in range(3):
+        tm()
+    t_ms = _time_events(tm, args.steps, stream)
+    extra["prefill"] = {
+        "invariant_tflops": round(achieved, 2),
+        "baseline_tflops": round(flop / (b_ms * 1e-3) / 1e12, 2),
+        "torch_linear_tflops": round(flop / (t_ms * 1e-3) / 1e12, 2),
+        "invariance_overhead_vs_baseline": round(kern_ms / b_ms - 1.0, 4),
+        "invariance_overhead_vs_torch": round(kern_ms / t_ms - 1.0, 4),
+    }
+    # bitwise: rows alone / in the batch, and 1 vs 8 partitions
+    ref = out.clone()
+    alone = torch.empty((8, N), dtype=torch.bfloat16, device="cuda")
+    rows = [0, 1, 127, 128, 2048, 4000, 4094, 4095]
+    ok = True
+    for i, r in enumerate(rows):
+        iso.gemm(A[r:r + 1].contiguous(), W, c, out=alone[i:i + 1], out_dtype=iso.BF16)
+    torch.cuda.synchronize()
+    ok &= bool(torch.equal(alone.view(torch.int16), ref[rows].view(torch.int16)))
+    out8 = torch.empty_like(out)
+    iso.gemm(A, W, c, out=out8, out_dtype=iso.BF16, partitions=8)
+    torch.cuda.synchronize()
+    ok &= bool(torch.equal(out8.view(torch.int16), ref.view(torch.int16)))
+    del out8, outb
+
+    if not args.quick:
+        # ---------------- invariance-sweep shape, 16 leaves
+        Ks = 4096
+        Ws = _dev(normal_bf16(401, (4096, Ks), 0.02))
+        As = _dev(normal_bf16(403, (4096, Ks), 1.0))
+        cs = iso.contract(16, 256, 0)
+        outs = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
+        ws8 = torch.empty(iso.gemm_workspace(cs, 4096, 4096, 8), dtype=torch.uint8, device="cuda")
+        g1 = lambda: iso.gemm(As, Ws, cs, out=outs)
+        g8 = lambda: iso.gemm(As, Ws, cs, out=outs, partitions=8, workspace=ws8)
+        g1()
+        ms1 = _time_events(g1, max(5, args.steps // 5), stream)
+        ref_s = outs.clone()
+        g8()
+        ms8 = _time_events(g8, max(5, args.steps // 5), stream)
+        ok &= bool(torch.equal(outs.view(torch.int32), ref_s.view(torch.int32)))
+        fs = 2.0 * 4096 * 4096 * Ks
+        extra["sweep"] = {"shape": "4096x4096x4096, 16 leaves of 256, fp32 out",
+                          "p1_tflops": round(fs / (ms1 * 1e-3) / 1e12, 2),
+                          "p8_tflops": round(fs / (ms8 * 1e-3) / 1e12, 2),
+                          "p1_ms": round(ms1, 4), "p8_ms": round(ms8, 4)}
+        del Ws, As, outs, ws8, ref_s
+
+        # ---------------- LM-head logprob
+        lm = make_config("lmhead")
+        H, Wv = _dev(lm["H"]), _dev(lm["Wvt"])
+        tok = torch.from_numpy(lm["tok"]).to("cuda")
+        cl = iso.contract(lm["leaves"], lm["K"] // lm["leaves"], iso.VOCAB_CHUNK)
+        lp = torch.empty(lm["M"], dtype=torch.float32, device="cuda")
+        wsl = torch.empty(iso.lmhead_workspace(cl, lm["M"], lm["V"], 1), dtype=torch.uint8,
+                          device="cuda")
+        run_lm = lambda: iso.lmhead_logprob(H, Wv, tok, cl, out=lp, workspace=wsl)
+        run_lm()
+        lm_ms = _time_events(run_lm, max(3, args.steps // 10), stream)
+        lm_flop = 2.0 * lm["M"] * lm["V"] * lm["K"]
+        lp_ref = lp.clone()
+        lp8 = torch.empty(8, dtype=torch.float32, device="cuda")
+        wsl8 = torch.empty(iso.lmhead_workspace(cl, 8, lm["V"], 1), dtype=torch.uint8, device="cuda")
+        iso.lmhead_logprob(H[4000:4008].contiguous(), Wv, tok[4000:4008].contiguous(), cl, out=lp8,
+                           workspace=wsl8)
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(lp8.view(torch.int32), lp_ref[4000:4008].view(torch.int32)))
+        extra["lmhead"] = {"shape": "8192 x 2048 x 151936, 8 leaves of 256, 1187 vocab chunks",
+                           "rows_per_s": round(lm["M"] / (lm_ms * 1e-3), 1),
+                           "ms": round(lm_ms, 4),
+                           "tflops": round(lm_flop / (lm_ms * 1e-3) / 1e12, 2),
+                           "mfma_frac": round(lm_flop / (lm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del H, Wv, tok, lp, wsl
+
+    extra["bitwise_pass"] = ok
+    line["bitwise_pass"] = ok
+    line["sub"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -190,6 +190,10 @@ const char *iso_status_str(iso_status s);
 /* Library version string, e.g. "iso 0.1.0 gfx950". */
 const char *iso_version(void);
 
+/* The HIP runtime's description of the last launch result of an entry point
+ * on the calling thread ("no error" after a successful launch). */
+const char *iso_last_launch_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -106,7 +106,7 @@ def make_config(name: str, rows: int | None = None) -> dict:
         return out
     if name == "sweep":
         out.update(Wt=normal_bf16(c["seeds"][0], (c["N"], c["K"]), c["sigma_w"]),
-                   probes=normal_bf16(c["seeds"][1], (c["probes"], c["K"]), c["sigma_a"]),
+                   probe_rows=normal_bf16(c["seeds"][1], (c["probes"], c["K"]), c["sigma_a"]),
                    filler=normal_bf16(c["seeds"][2], (4096, c["K"]), c["sigma_a"]),
                    placement_seed=c["seeds"][3])
         return out

@@ -15,6 +15,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# PyTorch bundles its own HIP runtime (SONAME libamdhip64.so.7).  Importing it
+# first makes libiso.so bind to that same runtime, so device pointers and
+# streams from torch are valid in the library; loading libiso.so first would
+# bring up a second runtime instance in the process.
+import torch  # noqa: F401  (load order matters)
+
 __all__ = [
     "IsoError", "Contract", "contract", "digest", "check_identity", "check_partitions",
     "gemm_workspace", "gemm", "gemm_baseline", "lmhead_workspace", "lmhead_logprob",
@@ -26,7 +32,7 @@ LIB_PATH = os.path.join(_PKG, "libiso.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m parallelism_invariant_numerics_amd.build` "
+        f"{LIB_PATH} is not built; run `python parallelism_invariant_numerics_amd/build.py` "
         "(the library has no non-HIP fallback)")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -53,6 +59,8 @@ class IsoError(RuntimeError):
         self.status = status
         self.name = _STATUS.get(status, str(status))
         msg = lib.iso_status_str(status).decode()
+        if self.name == "ISO_ERR_LAUNCH":
+            msg += ": " + lib.iso_last_launch_error().decode()
         super().__init__(f"{where}: {self.name} ({msg})")
 
 
@@ -75,6 +83,7 @@ _SIGS = {
                            _I),
     "iso_status_str": ([_I], ctypes.c_char_p),
     "iso_version": ([], ctypes.c_char_p),
+    "iso_last_launch_error": ([], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(lib, _name)

@@ -1,6 +1,6 @@
 """Build libiso.so (HIP kernels for gfx950 + the C-ABI host code) in-tree.
 
-    python -m parallelism_invariant_numerics_amd.build
+    python parallelism_invariant_numerics_amd/build.py
 
 hipcc cross-compiles for gfx950 without a GPU.  Device code is built with
 FP contraction off and without fast-math, so every kernel that shares a

@@ -43,7 +43,18 @@ int internal_parts(const iso_contract *c, int partitions)
     return lpp > kMaxLeavesPerTile ? (int)c->leaf_count / kMaxLeavesPerTile : partitions;
 }
 
-iso_status launch_status(hipError_t e) { return e == hipSuccess ? ISO_OK : ISO_ERR_LAUNCH; }
+thread_local hipError_t g_last_launch_error = hipSuccess;
+
+iso_status launch_status(hipError_t e)
+{
+    g_last_launch_error = e;
+    return e == hipSuccess ? ISO_OK : ISO_ERR_LAUNCH;
+}
+
+// The runtime's last-error slot may hold an error left by an earlier,
+// unrelated HIP call of the caller; clear it so a launch check reports only
+// this entry point's launches.
+void clear_stale_error() { (void)hipGetLastError(); }
 
 struct LmLayout {
     size_t stats, target, roots, total;
@@ -192,6 +203,7 @@ iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *
     if (need > 0 && (!workspace || workspace_bytes < need))
         return ISO_ERR_WORKSPACE;
 
+    clear_stale_error();
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lpp = (int)c->leaf_count / parts;
     const int bf16 = out_dtype == ISO_BF16;
@@ -203,7 +215,7 @@ iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *
                                              static_cast<const uint16_t *>(Wt), workspace, 2, M,
                                              N, K, lpp, (int)c->leaf_size, parts, st);
     if (e != hipSuccess)
-        return ISO_ERR_LAUNCH;
+        return launch_status(e);
     return launch_status(iso::launch_partition_combine(static_cast<const float *>(workspace), C,
                                                        bf16, M * N, parts, st));
 }
@@ -222,6 +234,7 @@ iso_status iso_gemm_baseline(const void *A, const void *Wt, void *C, uint32_t ou
     if (!A || !Wt || !C || !aligned16(A) || !aligned16(Wt))
         return ISO_ERR_ARG;
     // one leaf spanning all of K: a single accumulator, no tree
+    clear_stale_error();
     return launch_status(iso::launch_gemm_partials(
         static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Wt), C,
         out_dtype == ISO_BF16 ? 1 : 0, M, N, K, 1, (int)K, 1, static_cast<hipStream_t>(stream)));
@@ -260,6 +273,7 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
     if (!workspace || workspace_bytes < l.total || !aligned16(workspace))
         return ISO_ERR_WORKSPACE;
 
+    clear_stale_error();
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *ws = static_cast<char *>(workspace);
     float *stats = reinterpret_cast<float *>(ws + l.stats);
@@ -269,7 +283,7 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
         static_cast<const uint16_t *>(H), static_cast<const uint16_t *>(Wvt), tok, stats, target,
         roots, M, V, K, (int)c->leaf_count / parts, (int)c->leaf_size, parts, st);
     if (e != hipSuccess)
-        return ISO_ERR_LAUNCH;
+        return launch_status(e);
     return launch_status(iso::launch_lmhead_finish(stats, target, tok, logprob, M, V, st));
 }
 
@@ -290,5 +304,7 @@ const char *iso_status_str(iso_status s)
 }
 
 const char *iso_version(void) { return "iso 0.1.0 gfx950"; }
+
+const char *iso_last_launch_error(void) { return hipGetErrorString(g_last_launch_error); }
 
 }  // extern "C"

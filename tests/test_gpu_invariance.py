@@ -53,7 +53,7 @@ def _layouts(cfg):
 
 def test_invariance_sweep(sweep):
     cfg, c, dW = sweep
-    probes, filler = cfg["probes"], cfg["filler"]
+    probes, filler = cfg["probe_rows"], cfg["filler"]
     note("sweep reference: batch 1, P=1")
     ref = np.stack([_gemm(c, dW, probes[i:i + 1], 1)[0] for i in range(cfg["probes"])])
     # the reference itself against the oracle, on sampled columns
