@@ -51,16 +51,20 @@ def _dev(bits):
 
 
 def _time_events(fn, steps, stream):
-    """Average duration (ms) of fn() measured with HIP events on `stream`."""
+    """Average duration (ms) of one fn() call: HIP events on `stream` around
+    `steps` back-to-back calls (the launches queue up, so host-side call
+    overhead does not appear as idle GPU time between them)."""
     import torch
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record(stream)
-        fn()
-        ends[i].record(stream)
+    fn()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
 
 
 def _source_hash(files):

@@ -7,6 +7,8 @@
 // partition ("emulated rank") p of P owns leaves [p L/P, (p+1) L/P); its
 // workgroups write that subtree's root, and the combine kernel applies the
 // top log2(P) levels of the same tree, so every P gives the same bits.
+#include <type_traits>
+
 #include "gemm_core.hpp"
 #include "kernels.h"
 
@@ -24,51 +26,30 @@ struct GemmParams {
     int mode;             // OutMode
 };
 
-// Build the per-thread staging pointers of a dense tile.  Rows or columns
-// past the matrix edge are clamped to the last valid one: their products land
-// only in outputs that are never stored, and MFMA keeps outputs independent.
-__device__ __forceinline__ TileSrc dense_src(const uint16_t *A, const uint16_t *Wt, int64_t M,
-                                             int64_t N, int64_t K, int64_t m0, int64_t n0,
-                                             int64_t k0)
+template <class C, int LOG>
+__global__ __launch_bounds__(C::kThreads, 2) void gemm_leaf_kernel(GemmParams p)
 {
-    TileSrc s;
-    const int tid = threadIdx.x;
-    const int64_t kc = k0 + (tid & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t r = m0 + (tid >> 3) + 32 * i;
-        r = r < M ? r : M - 1;
-        s.a[i] = A + r * K + kc;
-        int64_t c = n0 + (tid >> 3) + 32 * i;
-        c = c < N ? c : N - 1;
-        s.b[i] = Wt + c * K + kc;
-    }
-    return s;
-}
-
-template <int LOG>
-__global__ __launch_bounds__(kThreads) void gemm_leaf_kernel(GemmParams p)
-{
-    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
     const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
     const int part = blockIdx.z;
 
-    TileSrc src = dense_src(p.A, p.Wt, p.M, p.N, p.K, m0, n0, part * p.k_per_part);
-    Acc root;
-    leaf_tree_mainloop<LOG>(src, p.stages_per_leaf, lds, root);
+    const Pipe pipe = make_pipe<C>(p.A + m0 * p.K, p.M - m0, p.Wt + n0 * p.K, p.N - n0, p.K,
+                                      part * p.k_per_part);
+    Acc<C> root;
+    leaf_tree_mainloop<C, LOG>(pipe, p.stages_per_leaf, lds, root);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / C::WC, wc = wave % C::WC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < C::JB; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + tile_row(lane, wr, i, r);
-                const int64_t col = n0 + tile_col(lane, wc, j);
+                const int64_t row = m0 + tile_row<C>(lane, wr, i, r);
+                const int64_t col = n0 + tile_col<C>(lane, wc, j);
                 if (row >= p.M || col >= p.N)
                     continue;
                 const float v = root.v[i][j][r];
@@ -103,12 +84,15 @@ __global__ __launch_bounds__(256) void partition_combine_kernel(const float *ws,
     }
 }
 
+// Trees of at most two leaves per workgroup fit the two-workgroups-per-CU
+// shape; deeper ones take the eight-wave shape.  Both give the same bits.
 template <int LOG>
 static hipError_t launch_leaf(const GemmParams &p, int parts, hipStream_t stream)
 {
+    using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
     dim3 grid(static_cast<unsigned>((p.N + BN - 1) / BN), static_cast<unsigned>((p.M + BM - 1) / BM),
               static_cast<unsigned>(parts));
-    hipLaunchKernelGGL(gemm_leaf_kernel<LOG>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_leaf_kernel<C, LOG>), grid, dim3(C::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -8,72 +8,144 @@
 // Mismatch in SkyRL", section "Achieving Parallelism Invariance", TP bullet:
 // contiguous K leaves, deterministic matrix-core products with FP32
 // accumulation, fixed binary tree.)  MFMA computes each output element from
-// its own A row and B column only, so neither the tile shape, nor the row's
-// position in the tile, nor the other rows change its bits.
+// its own A row and B column only, so neither the tile shape, nor the wave
+// layout, nor the row's position in the tile, nor the other rows change its
+// bits: the two launch shapes below give identical results.
 //
-// Tiling (gfx950): 256 threads = 4 wave64 in a 2 x 2 grid; workgroup tile
-// 128 x 128; wave tile 64 x 64 = 4 x 4 MFMA blocks of 16 x 16.  K is staged
-// through LDS 64 at a time (two MFMA k-steps), double buffered.  Both operands
-// are k-contiguous in HBM (A [M][K], Wt [N][K]); one LDS row is the 128-byte
-// k-slice of one matrix row, its eight 16-byte chunks XOR-swizzled by
-// (row & 7) so that the MFMA fragment reads (16 rows x one chunk) and the
-// staging writes (8 rows x 8 chunks) spread over all banks.
+// Tiling (gfx950): a workgroup computes a 128 x 128 output tile with its
+// waves in a 2 x WC grid (wave tile 64 x 128/WC, built from 16 x 16 MFMA
+// blocks).  Both operands are k-contiguous in HBM (A [M][K], Wt [N][K]).  K
+// moves through LDS 64 at a time ("stages") in a ring of 32 KiB stage buffers
+// filled by direct global-to-LDS buffer loads issued NBUF-1 stages ahead, so
+// no staging registers are needed.  One LDS row holds the 128-byte k-slice of
+// one matrix row; its eight 16-byte chunks are XOR-swizzled by (row & 7),
+// which keeps the 16-row fragment reads free of bank conflicts.  Rows past
+// the matrix edge read as zero (buffer range check) and are never stored.
+//
+// Launch shapes (both keep two waves on every SIMD, which the MFMA pipe needs
+// to stay busy across LDS and barrier waits):
+//   CfgWide: 8 waves (2 x 4, wave tile 64 x 32), one workgroup per CU, a
+//            four-stage ring (128 KiB).  Holds a 3- or 4-level register tree.
+//   CfgDual: 4 waves (2 x 2, wave tile 64 x 64), two workgroups per CU, a
+//            two-stage ring (64 KiB).  Register room for at most one tree
+//            level; the second workgroup hides the first one's waits.
+//
+// Fragment reads are issued ahead of the MFMAs that use them: the second
+// k-step's fragments of a stage load while the first k-step multiplies, and
+// the first k-step of the next stage loads while the previous stage's second
+// k-step multiplies.  The LDS reads and the waits are inline assembly so that
+// the compiler does not add conservative waits for the in-flight global-to-LDS
+// loads of later stages.
 //
 // The tree over the leaves of one workgroup is kept in registers as a
 // binary-counter stack: after leaf J, the running value absorbs the saved
 // left sibling at every level where bit b of J is 1, and is saved at the
-// first level where it is 0.  Depth log2(leaves) + 1 accumulator sets.
+// first level where it is 0.  Saved sums are parked in AGPRs.
 #pragma once
 
 #include <utility>
 
 #include "device_common.hpp"
 
+#define ISO_LDS __attribute__((address_space(3)))
+
 namespace iso {
 
 constexpr int BM = 128;
 constexpr int BN = 128;
 constexpr int BK = 64;
-constexpr int kThreads = 256;
-constexpr int kRowBytes = BK * 2;                        // 128 bytes per LDS row
-constexpr int kStageBytes = (BM + BN) * kRowBytes;        // 32 KiB per stage
-constexpr int kLdsBytes = 2 * kStageBytes;                // 64 KiB, double buffered
-constexpr int kMaxLogLeavesPerTile = 4;                   // register stack depth bound
+constexpr int kRowBytes = BK * 2;                    // 128 bytes per LDS row
+constexpr int kStageBytes = (BM + BN) * kRowBytes;   // 32 KiB per stage
+constexpr int kBOffset = BM * kRowBytes;             // B tile inside a stage
 
+template <int WC_, int NBUF_>
+struct TileCfg {
+    static constexpr int WR = 2;
+    static constexpr int WC = WC_;
+    static constexpr int kWaves = WR * WC;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int IB = BM / WR / 16;  // 16-row blocks per wave
+    static constexpr int JB = BN / WC / 16;  // 16-column blocks per wave
+    static constexpr int NBUF = NBUF_;
+    static constexpr int kLdsBytes = NBUF * kStageBytes;
+    static constexpr int kDma = BM / kWaves / 8;  // buffer loads per operand per wave per stage
+};
+using CfgWide = TileCfg<4, 4>;
+using CfgDual = TileCfg<2, 2>;
+
+template <class C>
 struct Acc {
-    f32x4 v[4][4];
+    f32x4 v[C::IB][C::JB];
 };
 
-__device__ __forceinline__ void acc_zero(Acc &a)
+// One 32-deep MFMA k-step's operands: A row blocks i and B column blocks j.
+template <class C>
+struct Frags {
+    bf16x8 a[C::IB];
+    bf16x8 b[C::JB];
+};
+
+template <class C>
+__device__ __forceinline__ void acc_zero(Acc<C> &a)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < C::JB; ++j)
             a.v[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// dst = left + right, element by element (one FP32 add, round to nearest).
-__device__ __forceinline__ void acc_add(Acc &dst, const Acc &left, const Acc &right)
+template <class C>
+__device__ __forceinline__ void mfma_step(Acc<C> &acc, const Frags<C> &f)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dst.v[i][j] = left.v[i][j] + right.v[i][j];
+        for (int j = 0; j < C::JB; ++j)
+            acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc.v[i][j], 0,
+                                                                  0, 0);
+}
+
+// Saved subtree sums are parked in the accumulation registers (AGPRs); these
+// empty asm statements only pin the register class (values pass unchanged).
+template <class C>
+__device__ __forceinline__ void park(Acc<C> &dst, const Acc<C> &src)
+{
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::JB; ++j) {
+            f32x4 t = src.v[i][j];
+            asm volatile("" : "=a"(t) : "0"(t));
+            dst.v[i][j] = t;
+        }
+}
+
+// v = left + v element by element (left sibling = lower leaf indices).
+template <class C>
+__device__ __forceinline__ void unpark_add(Acc<C> &v, const Acc<C> &left)
+{
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::JB; ++j) {
+            f32x4 t = left.v[i][j];
+            asm volatile("" : "=v"(t) : "0"(t));
+            v.v[i][j] = t + v.v[i][j];
+        }
 }
 
 // Fold one finished leaf (index J within the tile's leaf block) into the
 // register tree.  After the last leaf, `v` holds the block's subtree root.
-template <int LOG, int J, int B>
-__device__ __forceinline__ void tree_push(Acc (&stk)[LOG > 0 ? LOG : 1], Acc &v)
+template <class C, int LOG, int J, int B>
+__device__ __forceinline__ void tree_push(Acc<C> (&stk)[LOG > 0 ? LOG : 1], Acc<C> &v)
 {
     if constexpr (B < LOG) {
         if constexpr (((J >> B) & 1) != 0) {
-            acc_add(v, stk[B], v);  // left sibling (lower leaf indices) + right
-            tree_push<LOG, J, B + 1>(stk, v);
+            unpark_add(v, stk[B]);
+            tree_push<C, LOG, J, B + 1>(stk, v);
         } else {
-            stk[B] = v;
+            park(stk[B], v);
         }
     }
 }
@@ -90,116 +162,198 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl(static_cast<F &&>(f), std::make_integer_sequence<int, N>{});
 }
 
-// Per-thread global sources: this thread stages rows (tid/8 + 32 i), i < 4,
-// of both operand tiles, 16-byte chunk (tid & 7) of each 64-wide k-slice.
-// Pointers already include the chunk offset and the tile's first k.
-struct TileSrc {
-    const uint16_t *a[4];
-    const uint16_t *b[4];
+// ------------------------------------------------------------------ sources
+
+// A 128-row operand tile: rows [0, rows) of a k-contiguous matrix starting at
+// `base`, `K` elements per row.  Rows at or past `rows` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t rows,
+                                                            int64_t K)
+{
+    int64_t bytes = rows * K * 2;
+    if (bytes > 0xffffffffLL)
+        bytes = 0xffffffffLL;
+    if (bytes < 0)
+        bytes = 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0,
+                                             (int)(uint32_t)bytes, 0x00020000);
+}
+
+// Per-thread state of the stage pipeline of one tile (kDma <= 4 entries of
+// voff are used).
+constexpr int kMaxDma = 4;
+struct Pipe {
+    __amdgpu_buffer_rsrc_t ra, rb;  // A tile rows, B tile rows
+    uint32_t voff[kMaxDma];         // this lane's byte offsets for its DMA rows
+    uint32_t kbyte0;                // byte offset of the tile's first k (partition start)
 };
 
-struct StageRegs {
-    u32x4 a[4];
-    u32x4 b[4];
-};
-
-__device__ __forceinline__ void stage_load(StageRegs &r, const TileSrc &src, int64_t k)
+// Lane l of wave w stages, for i < kDma, row r = kDma*8 w + 8 i + (l >> 3)
+// and the global 16-byte chunk c = (l & 7) ^ (r & 7) into LDS slot (r, l & 7)
+// of both the A and the B tile: one buffer load fills 8 consecutive LDS rows,
+// 1 KiB, lane by lane.  A rows [rowsA, 128) and B rows [rowsB, 128) are past
+// the matrix edge and read as zero.
+template <class C>
+__device__ __forceinline__ Pipe make_pipe(const uint16_t *A_tile, int64_t rowsA,
+                                             const uint16_t *B_tile, int64_t rowsB, int64_t K,
+                                             int64_t k0)
 {
+    static_assert(C::kDma <= kMaxDma, "too many loads per wave");
+    Pipe p;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    p.ra = tile_rsrc(A_tile, rowsA < BM ? rowsA : BM, K);
+    p.rb = tile_rsrc(B_tile, rowsB < BN ? rowsB : BN, K);
+    const uint32_t c = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.a[i] = *reinterpret_cast<const u32x4 *>(src.a[i] + k);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.b[i] = *reinterpret_cast<const u32x4 *>(src.b[i] + k);
-}
-
-__device__ __forceinline__ void stage_store(const StageRegs &r, char *stage, int tid)
-{
-    const int c = tid & 7;
-    const int sw = ((c ^ ((tid >> 3) & 7)) << 4);
-    char *As = stage;
-    char *Bs = stage + BM * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 32 * i;
-        *reinterpret_cast<u32x4 *>(As + row * kRowBytes + sw) = r.a[i];
-        *reinterpret_cast<u32x4 *>(Bs + row * kRowBytes + sw) = r.b[i];
+    for (int i = 0; i < C::kDma; ++i) {
+        const uint32_t r = C::kDma * 8 * w + 8 * i + (lane >> 3);
+        p.voff[i] = (uint32_t)((int64_t)r * K * 2) + c * 16;
     }
+    p.kbyte0 = (uint32_t)(k0 * 2);
+    return p;
 }
 
-// Two MFMA k-steps (k 0..31, then 32..63 of the stage) into acc.
-__device__ __forceinline__ void stage_mfma(Acc &acc, const char *stage, int lane, int wr, int wc)
+template <class C>
+__device__ __forceinline__ void stage_dma(const Pipe &p, char *lds, int st, int buf)
 {
-    const char *As = stage + (wr * 64 + (lane & 15)) * kRowBytes;
-    const char *Bs = stage + BM * kRowBytes + (wc * 64 + (lane & 15)) * kRowBytes;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t soff = p.kbyte0 + (uint32_t)st * (BK * 2);
+    char *dst = lds + buf * kStageBytes + w * C::kDma * 8 * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int chunk = (((s * 4) + (lane >> 4)) ^ (lane & 7)) << 4;
-        bf16x8 a[4], b[4];
+    for (int i = 0; i < C::kDma; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(p.ra, (ISO_LDS void *)(dst + i * 8 * kRowBytes),
+                                                 16, p.voff[i], soff, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = *reinterpret_cast<const bf16x8 *>(As + i * 16 * kRowBytes + chunk);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = *reinterpret_cast<const bf16x8 *>(Bs + j * 16 * kRowBytes + chunk);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc.v[i][j], 0,
-                                                                      0, 0);
-    }
+    for (int i = 0; i < C::kDma; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            p.rb, (ISO_LDS void *)(dst + kBOffset + i * 8 * kRowBytes), 16, p.voff[i], soff, 0,
+            0);
 }
 
-// The contraction of one tile over 2^LOG leaves of `stages_per_leaf` * 64
-// columns of K each.  On return `root` holds the subtree root in the MFMA
-// output layout; every thread has passed a final barrier, so `lds` may be
-// reused by the caller.
-template <int LOG>
-__device__ __forceinline__ void leaf_tree_mainloop(const TileSrc &src, int stages_per_leaf,
-                                                   char *lds, Acc &root)
+// Wait until at most `pending` later stages of this wave's buffer loads
+// (2 kDma loads per stage) are still in flight, then synchronise the
+// workgroup.
+template <class C>
+__device__ __forceinline__ void stage_barrier(int pending)
+{
+    constexpr int D = 2 * C::kDma;
+    if (pending >= 2)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * D) : "memory");
+    else if (pending == 1)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(D) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Issue the LDS reads of one k-step's fragments (no wait).
+template <class C>
+__device__ __forceinline__ void frag_read(Frags<C> &f, uint32_t addr_a, uint32_t addr_b)
+{
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+        asm volatile("ds_read_b128 %0, %1 offset:%2"
+                     : "=&v"(f.a[i])
+                     : "v"(addr_a), "n"(i * 16 * kRowBytes));
+#pragma unroll
+    for (int j = 0; j < C::JB; ++j)
+        asm volatile("ds_read_b128 %0, %1 offset:%2"
+                     : "=&v"(f.b[j])
+                     : "v"(addr_b), "n"(j * 16 * kRowBytes));
+}
+
+// Wait for all LDS reads of this wave; the fragments become usable after it.
+template <class C>
+__device__ __forceinline__ void frag_wait(Frags<C> &f)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+        asm volatile("" : "+v"(f.a[i]));
+#pragma unroll
+    for (int j = 0; j < C::JB; ++j)
+        asm volatile("" : "+v"(f.b[j]));
+}
+
+// The contraction of one tile over 2^LOG leaves of `spl` stages (64 columns
+// of K) each.  On return `root` holds the subtree root in the MFMA output
+// layout, every buffer load has landed and all waves have passed a final
+// barrier, so `lds` may be reused by the caller.
+template <class C, int LOG>
+__device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char *lds,
+                                                   Acc<C> &root)
 {
     constexpr int LP = 1 << LOG;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wr = wave >> 1;
-    const int wc = wave & 1;
-    const int nst = LP * stages_per_leaf;
+    constexpr int NB = C::NBUF;
+    const int nst = LP * spl;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wr = wave / C::WC;
+    const int wc = wave % C::WC;
 
-    StageRegs regs;
-    stage_load(regs, src, 0);
-    stage_store(regs, lds, tid);
-    __syncthreads();
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(ISO_LDS char *)lds;
+    const uint32_t ch0 = (uint32_t)(((lane >> 4) ^ (lane & 7)) << 4);
+    const uint32_t ch1 = ch0 ^ 64u;  // chunks 4..7 of the row: second k-step
+    const uint32_t rowa = (uint32_t)(wr * (BM / C::WR) + (lane & 15)) * kRowBytes;
+    const uint32_t rowb =
+        (uint32_t)kBOffset + (uint32_t)(wc * (BN / C::WC) + (lane & 15)) * kRowBytes;
 
-    Acc stk[LOG > 0 ? LOG : 1];
-    Acc acc;
+#pragma unroll
+    for (int s = 0; s < NB - 1; ++s)
+        if (s < nst)
+            stage_dma<C>(p, lds, s, s);
+
+    Acc<C> stk[LOG > 0 ? LOG : 1];
+    Acc<C> acc;
+    acc_zero(acc);
+    Frags<C> f0, f1;
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+        f1.a[i] = bf16x8{};
+#pragma unroll
+    for (int j = 0; j < C::JB; ++j)
+        f1.b[j] = bf16x8{};
     int st = 0;
-    static_for<LP>([&](auto J) {
-        acc_zero(acc);
-        for (int s = 0; s < stages_per_leaf; ++s, ++st) {
-            const bool more = st + 1 < nst;
-            if (more)
-                stage_load(regs, src, static_cast<int64_t>(st + 1) * BK);
-            stage_mfma(acc, lds + (st & 1) * kStageBytes, lane, wr, wc);
-            if (more)
-                stage_store(regs, lds + ((st + 1) & 1) * kStageBytes, tid);
-            __syncthreads();
+    static_for<LP>([&](auto Jc) {
+        constexpr int J = decltype(Jc)::value;
+        for (int s = 0; s < spl; ++s, ++st) {
+            frag_wait(f1);  // previous stage's reads done before its buffer is recycled
+            const int ahead = nst - 1 - st;
+            stage_barrier<C>(ahead < NB - 2 ? ahead : NB - 2);
+            if (st + NB - 1 < nst)
+                stage_dma<C>(p, lds, st + NB - 1, (st + NB - 1) % NB);
+            const uint32_t base = lds_addr + (uint32_t)(st % NB) * kStageBytes;
+            frag_read(f0, base + rowa + ch0, base + rowb + ch0);
+            if (st > 0) {
+                mfma_step(acc, f1);  // second k-step of the previous stage
+                if constexpr (J > 0) {
+                    if (s == 0) {  // the previous stage closed leaf J - 1
+                        tree_push<C, LOG, J - 1, 0>(stk, acc);
+                        acc_zero(acc);
+                    }
+                }
+            }
+            frag_wait(f0);
+            frag_read(f1, base + rowa + ch1, base + rowb + ch1);
+            mfma_step(acc, f0);
         }
-        tree_push<LOG, decltype(J)::value, 0>(stk, acc);
-        if constexpr (decltype(J)::value == LP - 1)
-            root = acc;
     });
+    frag_wait(f1);
+    mfma_step(acc, f1);
+    tree_push<C, LOG, LP - 1, 0>(stk, acc);
+    root = acc;
+    __builtin_amdgcn_s_barrier();
 }
 
 // Row and column (within the 128 x 128 tile) of acc.v[i][j][r] for this lane.
+template <class C>
 __device__ __forceinline__ int tile_row(int lane, int wr, int i, int r)
 {
-    return wr * 64 + i * 16 + (lane >> 4) * 4 + r;
+    return wr * (BM / C::WR) + i * 16 + (lane >> 4) * 4 + r;
 }
+template <class C>
 __device__ __forceinline__ int tile_col(int lane, int wc, int j)
 {
-    return wc * 64 + j * 16 + (lane & 15);
+    return wc * (BN / C::WC) + j * 16 + (lane & 15);
 }
 
 // Fixed tree over P partition roots (P = 1, 2, 4, 8), lower index left.

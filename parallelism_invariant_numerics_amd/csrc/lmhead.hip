@@ -20,6 +20,8 @@
 // The logits never leave registers on the fused path (one partition).  With
 // several partitions the partition roots of the logits go through the
 // workspace and the same epilogue function runs on their folded values.
+#include <type_traits>
+
 #include "gemm_core.hpp"
 #include "kernels.h"
 
@@ -38,29 +40,54 @@ struct LmArgs {
     int stages_per_leaf;
 };
 
-// Chunk statistics of one 128 x 128 logit tile held in MFMA layout.
-// `red` is LDS scratch of at least 512 floats, free for use on entry.
-__device__ __forceinline__ void chunk_stats_epilogue(const Acc &z, int64_t m0, int64_t n0,
+// Chunk statistics of one 128 x 128 logit tile held in MFMA layout.  The
+// chunk's columns are spread over the C::WC waves of a tile row; every launch
+// shape reduces them with the same balanced tree in column order (16-column
+// blocks by lane butterfly, then blocks inside a wave, then waves), so the
+// bits do not depend on the shape.  `red` is LDS scratch of at least
+// 2 * C::WC * 128 floats, free for use on entry.
+template <class C>
+__device__ __forceinline__ float tree_blocks(const float (&b)[C::JB])
+{
+    if constexpr (C::JB == 4)
+        return (b[0] + b[1]) + (b[2] + b[3]);
+    else
+        return b[0] + b[1];
+}
+
+template <class C>
+__device__ __forceinline__ float tree_waves(const float *red, int rt)
+{
+    if constexpr (C::WC == 4)
+        return (red[rt] + red[128 + rt]) + (red[256 + rt] + red[384 + rt]);
+    else
+        return red[rt] + red[128 + rt];
+}
+
+template <class C>
+__device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0, int64_t n0,
                                                      const LmArgs &a, float *red)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / C::WC, wc = wave % C::WC;
     const int64_t chunk = n0 / kChunk;
+    float *red_m = red;
+    float *red_s = red + C::WC * 128;
 
-    bool colv[4];
+    bool colv[C::JB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        colv[j] = n0 + tile_col(lane, wc, j) < a.V;
+    for (int j = 0; j < C::JB; ++j)
+        colv[j] = n0 + tile_col<C>(lane, wc, j) < a.V;
 
-    // half-chunk (64 columns) maxima per row, then the chunk maximum
+    // per-wave maxima per row, then the chunk maximum (exact, order-free)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float m = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < C::JB; ++j)
                 if (colv[j])
                     m = fmaxf(m, z.v[i][j][r]);
             m = fmaxf(m, shfl_xor(m, 1));
@@ -68,27 +95,31 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc &z, int64_t m0, i
             m = fmaxf(m, shfl_xor(m, 4));
             m = fmaxf(m, shfl_xor(m, 8));
             if ((lane & 15) == 0)
-                red[wc * 128 + tile_row(lane, wr, i, r)] = m;
+                red_m[wc * 128 + tile_row<C>(lane, wr, i, r)] = m;
         }
     __syncthreads();
 
-    float cm[4][4];
+    float cm[C::IB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int rt = tile_row(lane, wr, i, r);
-            cm[i][r] = fmaxf(red[rt], red[128 + rt]);
+            const int rt = tile_row<C>(lane, wr, i, r);
+            float m = red_m[rt];
+#pragma unroll
+            for (int q = 1; q < C::WC; ++q)
+                m = fmaxf(m, red_m[q * 128 + rt]);
+            cm[i][r] = m;
         }
 
     // exp-sums: 16-column blocks by lane butterfly, then blocks, then waves
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            float blk[4];
+            float blk[C::JB];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < C::JB; ++j) {
                 float e = colv[j] ? exp_neg(z.v[i][j][r] - cm[i][r]) : 0.0f;
                 e = e + shfl_xor(e, 1);
                 e = e + shfl_xor(e, 2);
@@ -96,95 +127,84 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc &z, int64_t m0, i
                 e = e + shfl_xor(e, 8);
                 blk[j] = e;
             }
-            const float half = (blk[0] + blk[1]) + (blk[2] + blk[3]);
+            const float part = tree_blocks<C>(blk);
             if ((lane & 15) == 0)
-                red[256 + wc * 128 + tile_row(lane, wr, i, r)] = half;
+                red_s[wc * 128 + tile_row<C>(lane, wr, i, r)] = part;
         }
     __syncthreads();
 
     if (wc == 0 && (lane & 15) == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < C::IB; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int rt = tile_row(lane, wr, i, r);
+                const int rt = tile_row<C>(lane, wr, i, r);
                 const int64_t row = m0 + rt;
                 if (row < a.M) {
-                    const float s = red[256 + rt] + red[256 + 128 + rt];
                     float *st = a.stats + (row * a.nchunk + chunk) * 2;
                     st[0] = cm[i][r];
-                    st[1] = s;
+                    st[1] = tree_waves<C>(red_s, rt);
                 }
             }
     }
 
     // the sampled token's logit: written by the one lane that holds it
+    constexpr int WCOLS = BN / C::WC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t row = m0 + tile_row(lane, wr, i, r);
+            const int64_t row = m0 + tile_row<C>(lane, wr, i, r);
             if (row >= a.M)
                 continue;
             const int64_t t = a.tok[row];
-            const int64_t rel = t - n0 - wc * 64 - (lane & 15);
-            if (rel >= 0 && rel < 64 && (rel & 15) == 0 && t < a.V) {
+            const int64_t rel = t - n0 - wc * WCOLS - (lane & 15);
+            if (rel >= 0 && rel < WCOLS && (rel & 15) == 0 && t < a.V) {
                 const int j = static_cast<int>(rel >> 4);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
+                for (int jj = 0; jj < C::JB; ++jj)
                     if (jj == j)
                         a.target[row] = z.v[i][jj][r];
             }
         }
 }
 
-template <int LOG>
-__global__ __launch_bounds__(kThreads) void lmhead_fused_kernel(LmArgs a)
+template <class C, int LOG>
+__global__ __launch_bounds__(C::kThreads, 2) void lmhead_fused_kernel(LmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
 
-    TileSrc src;
-    {
-        const int tid = threadIdx.x;
-        const int64_t kc = (tid & 7) * 8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int64_t r = m0 + (tid >> 3) + 32 * i;
-            r = r < a.M ? r : a.M - 1;
-            src.a[i] = a.H + r * a.K + kc;
-            int64_t c = n0 + (tid >> 3) + 32 * i;
-            c = c < a.V ? c : a.V - 1;
-            src.b[i] = a.Wvt + c * a.K + kc;
-        }
-    }
-    Acc z;
-    leaf_tree_mainloop<LOG>(src, a.stages_per_leaf, lds, z);
-    chunk_stats_epilogue(z, m0, n0, a, reinterpret_cast<float *>(lds));
+    const Pipe pipe =
+        make_pipe<C>(a.H + m0 * a.K, a.M - m0, a.Wvt + n0 * a.K, a.V - n0, a.K, 0);
+    Acc<C> z;
+    leaf_tree_mainloop<C, LOG>(pipe, a.stages_per_leaf, lds, z);
+    chunk_stats_epilogue<C>(z, m0, n0, a, reinterpret_cast<float *>(lds));
 }
 
 // Several partitions: fold the partition roots of the logits with the top
 // tree levels, in the MFMA layout, then the same epilogue.
 template <int P>
-__global__ __launch_bounds__(kThreads) void lmhead_roots_kernel(LmArgs a)
+__global__ __launch_bounds__(CfgDual::kThreads) void lmhead_roots_kernel(LmArgs a)
 {
-    __shared__ float red[512];
+    using C = CfgDual;
+    __shared__ float red[2 * C::WC * 128];
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / C::WC, wc = wave % C::WC;
     const int64_t MV = a.M * a.V;
-    Acc z;
+    Acc<C> z;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < C::JB; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                int64_t row = m0 + tile_row(lane, wr, i, r);
-                int64_t col = n0 + tile_col(lane, wc, j);
+                int64_t row = m0 + tile_row<C>(lane, wr, i, r);
+                int64_t col = n0 + tile_col<C>(lane, wc, j);
                 row = row < a.M ? row : a.M - 1;
                 col = col < a.V ? col : a.V - 1;
                 float rv[P];
@@ -193,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_roots_kernel(LmArgs a)
                     rv[q] = a.roots[q * MV + row * a.V + col];
                 z.v[i][j][r] = fold_roots<P>(rv);
             }
-    chunk_stats_epilogue(z, m0, n0, a, red);
+    chunk_stats_epilogue<C>(z, m0, n0, a, red);
 }
 
 // Per row: balanced tree over the chunk statistics in chunk order, then
@@ -260,8 +280,9 @@ __global__ __launch_bounds__(256) void lmhead_finish_kernel(const float *stats,
 template <int LOG>
 static hipError_t launch_fused(const LmArgs &a, hipStream_t stream)
 {
+    using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
     dim3 grid(static_cast<unsigned>((a.M + BM - 1) / BM), static_cast<unsigned>(a.nchunk));
-    hipLaunchKernelGGL(lmhead_fused_kernel<LOG>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((lmhead_fused_kernel<C, LOG>), grid, dim3(C::kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -298,9 +319,9 @@ hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int
         return e;
     dim3 grid(static_cast<unsigned>((M + BM - 1) / BM), static_cast<unsigned>(a.nchunk));
     switch (parts) {
-    case 2: hipLaunchKernelGGL(lmhead_roots_kernel<2>, grid, dim3(kThreads), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(lmhead_roots_kernel<4>, grid, dim3(kThreads), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(lmhead_roots_kernel<8>, grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(lmhead_roots_kernel<2>, grid, dim3(CfgDual::kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(lmhead_roots_kernel<4>, grid, dim3(CfgDual::kThreads), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(lmhead_roots_kernel<8>, grid, dim3(CfgDual::kThreads), 0, stream, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
