@@ -7,10 +7,11 @@ One step is one invariant GEMM of the prefill-shaped linear layer
 along K, FP32 accumulation and fixed tree, bf16 output) with its inputs
 resident in HBM; ``value`` is TFLOP/s (2 M N K per step).  The same run also
 times, as sub-measurements reported in the JSON line: the non-invariant
-comparison kernel and torch.matmul on the same shape, the invariance-sweep
-shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8 partitions, and the LM-head
-logprob workload (8192 rows x 2048 x 151936 vocabulary) in rows/s, plus a
-bitwise invariance check.  Prints ONE JSON line.
+comparison kernel and torch's linear layer on the same shape, the
+invariance-sweep shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8
+partitions, the LM-head logprob workload (8192 rows x 2048 x 151936
+vocabulary) in rows/s, the MoE FFN block (4096 tokens, 128 experts, top-8),
+plus bitwise invariance checks.  Prints ONE JSON line.
 
 Inputs are seeded synthetic data with the workloads' shapes and
 distributions (no dataset or trained weights are involved).
@@ -251,6 +252,34 @@ def main():
                            "tflops": round(lm_flop / (lm_ms * 1e-3) / 1e12, 2),
                            "mfma_frac": round(lm_flop / (lm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del H, Wv, tok, lp, wsl
+
+        # ---------------- MoE FFN block with the routing-order combine
+        mc = make_config("moe")
+        T, Hd, E, I, k = mc["T"], mc["H"], mc["E"], mc["I"], mc["top_k"]
+        X = _dev(mc["X"])
+        lgt = torch.from_numpy(mc["logits"]).to("cuda")
+        Wg, Wu, Wd = _dev(mc["Wg"]), _dev(mc["Wu"]), _dev(mc["Wd"])
+        cg = iso.contract(mc["leaves_gate_up"], Hd // mc["leaves_gate_up"], 0)
+        cd = iso.contract(mc["leaves_down"], I // mc["leaves_down"], 0)
+        y = torch.empty((T, Hd), dtype=torch.float32, device="cuda")
+        wsm = torch.empty(iso.moe_workspace(T, Hd, E, I, k), dtype=torch.uint8, device="cuda")
+        run_moe = lambda: iso.moe_combine(X, lgt, Wg, Wu, Wd, k, cg, cd, out=y, workspace=wsm)
+        run_moe()
+        moe_ms = _time_events(run_moe, max(3, args.steps // 5), stream)
+        y_ref = y.clone()
+        rev = torch.arange(T - 1, -1, -1, device="cuda")
+        yr = torch.empty_like(y)
+        iso.moe_combine(X[rev].contiguous(), lgt[rev].contiguous(), Wg, Wu, Wd, k, cg, cd, out=yr,
+                        workspace=wsm)
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(yr.view(torch.int32), y_ref[rev].view(torch.int32)))
+        moe_flop = 2.0 * T * k * (2 * Hd * I + I * Hd)
+        extra["moe"] = {"shape": "4096 tokens, hidden 2048, 128 experts, top-8, SwiGLU 512, "
+                                 "4 leaves (gate/up 4x512, down 4x128)",
+                        "ms": round(moe_ms, 4),
+                        "tokens_per_s": round(T / (moe_ms * 1e-3), 1),
+                        "tflops": round(moe_flop / (moe_ms * 1e-3) / 1e12, 2)}
+        del X, lgt, Wg, Wu, Wd, y, wsm, yr
 
     extra["bitwise_pass"] = ok
     line["bitwise_pass"] = ok

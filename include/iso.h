@@ -184,6 +184,49 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
                               int64_t K, int partitions, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* Byte offsets of the MoE workspace regions, for inspection of the stages.
+ *   idx    int32 [T][top_k]   expert ids in routing order
+ *   gate   float [T][top_k]   renormalised gates in routing order
+ *   h      bf16  [T][top_k][I] SwiGLU activations
+ *   e      float [T][top_k][H] expert outputs before the combine
+ * The remaining bytes up to `total` hold the per-expert buckets and the
+ * work list.  Returns ISO_ERR_ARG / ISO_ERR_SHAPE for arguments
+ * iso_moe_combine would reject for those reasons. */
+typedef struct iso_moe_layout {
+    size_t idx, gate, h, e, total;
+} iso_moe_layout;
+
+iso_status iso_moe_layout_of(int64_t T, int64_t H, int64_t E, int64_t I, int top_k,
+                             iso_moe_layout *out);
+
+/* Workspace bytes iso_moe_combine needs; (size_t)-1 for bad arguments. */
+size_t iso_moe_workspace(int64_t T, int64_t H, int64_t E, int64_t I, int top_k);
+
+/*
+ * MoE FFN with a fixed routing-order combine ([AGL] "Achieving Parallelism
+ * Invariance", EP bullet: expert outputs are combined in a fixed routing
+ * order rather than rank order; [KTB] section 9).
+ *   route:   per token, softmax over E FP32 router logits; the top_k experts
+ *            by (logit descending, expert id ascending) -- the routing
+ *            order; gates = their probabilities renormalised to sum to one.
+ *   experts: per (token, slot) with expert e: G = x Wg[e], U = x Wu[e]
+ *            (gate_up contract, K = H), h = bf16(silu(G) * U),
+ *            out = h Wd[e] (down contract, K = I), all FP32 leaf/tree GEMMs.
+ *   combine: y = g_0 out_0, then y = y + g_k out_k for k = 1..top_k-1,
+ *            FP32, each product rounded before its add.
+ * Layouts: X bf16 [T][H]; router_logits float [T][E]; Wg, Wu bf16 [E][I][H];
+ * Wd bf16 [E][H][I]; Y float [T][H].  Each token's bits do not depend on the
+ * other tokens in the batch or their order.  Router logits must be finite.
+ * Limits: 1 <= E <= 1024, 1 <= top_k <= min(16, E), leaf_count <= 16 in both
+ * contracts, T * top_k < 2^31, T * H * 2 and T * top_k * I * 2 below 2^32
+ * bytes.  X, the weights and Y must be 16-byte aligned.
+ */
+iso_status iso_moe_combine(const iso_contract *gate_up, const iso_contract *down,
+                           const void *X, const float *router_logits, const void *Wg,
+                           const void *Wu, const void *Wd, float *Y, int64_t T, int64_t H,
+                           int64_t E, int64_t I, int top_k, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *iso_status_str(iso_status s);
 

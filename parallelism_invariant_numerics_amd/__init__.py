@@ -24,6 +24,7 @@ import torch  # noqa: F401  (load order matters)
 __all__ = [
     "IsoError", "Contract", "contract", "digest", "check_identity", "check_partitions",
     "gemm_workspace", "gemm", "gemm_baseline", "lmhead_workspace", "lmhead_logprob",
+    "moe_workspace", "moe_layout", "moe_combine", "moe_stages",
     "lib", "LIB_PATH", "F32", "BF16", "VOCAB_CHUNK", "version",
 ]
 
@@ -81,6 +82,10 @@ _SIGS = {
     "iso_lmhead_workspace": ([_CP, _I64, _I64, _I], ctypes.c_size_t),
     "iso_lmhead_logprob": ([_CP, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P],
                            _I),
+    "iso_moe_layout_of": ([_I64, _I64, _I64, _I64, _I, _P], _I),
+    "iso_moe_workspace": ([_I64, _I64, _I64, _I64, _I], ctypes.c_size_t),
+    "iso_moe_combine": ([_CP, _CP, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P,
+                         ctypes.c_size_t, _P], _I),
     "iso_status_str": ([_I], ctypes.c_char_p),
     "iso_version": ([], ctypes.c_char_p),
     "iso_last_launch_error": ([], ctypes.c_char_p),
@@ -245,3 +250,61 @@ def lmhead_logprob(H, Wvt, tok, c: Contract, *, out=None, partitions: int = 1,
                                None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
         "iso_lmhead_logprob")
     return out
+
+
+class MoeLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "gate", "h", "e", "total")]
+
+
+def moe_layout(T: int, H: int, E: int, I: int, top_k: int) -> MoeLayout:
+    out = MoeLayout()
+    _ok(lib.iso_moe_layout_of(T, H, E, I, top_k, ctypes.byref(out)), "iso_moe_layout_of")
+    return out
+
+
+def moe_workspace(T: int, H: int, E: int, I: int, top_k: int) -> int:
+    n = lib.iso_moe_workspace(T, H, E, I, top_k)
+    if n == _BAD_SIZE:
+        raise IsoError(1, "iso_moe_workspace")
+    return n
+
+
+def moe_combine(X, router_logits, Wg, Wu, Wd, top_k: int, gate_up: Contract, down: Contract, *,
+                out=None, workspace=None, stream=None):
+    """MoE FFN with the fixed routing-order combine.  X [T][H] bf16, logits
+    [T][E] fp32, Wg/Wu [E][I][H], Wd [E][H][I] bf16.  Returns Y [T][H] fp32."""
+    torch = _torch()
+    T, H = X.shape
+    E, I, H2 = Wg.shape
+    if H2 != H or tuple(Wu.shape) != (E, I, H) or tuple(Wd.shape) != (E, H, I):
+        raise ValueError("weight shapes must be Wg/Wu [E][I][H], Wd [E][H][I]")
+    if tuple(router_logits.shape) != (T, E):
+        raise ValueError("router logits must be [T][E]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=X.device)
+    need = moe_workspace(T, H, E, I, top_k)
+    ws, wsb = _workspace(need, X.device, workspace)
+    _ok(lib.iso_moe_combine(ctypes.byref(gate_up), ctypes.byref(down), _bf16_ptr(X, "X"),
+                            _dev_ptr(router_logits, "router_logits", torch.float32),
+                            _bf16_ptr(Wg, "Wg"), _bf16_ptr(Wu, "Wu"), _bf16_ptr(Wd, "Wd"),
+                            _dev_ptr(out, "out", torch.float32), T, H, E, I, top_k,
+                            None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
+        "iso_moe_combine")
+    return out
+
+
+def moe_stages(workspace, T: int, H: int, E: int, I: int, top_k: int) -> dict:
+    """Views of the stage outputs left in a MoE workspace: idx [T][k] int32,
+    gate [T][k] fp32, h [T][k][I] bf16, e [T][k][H] fp32."""
+    torch = _torch()
+    lay = moe_layout(T, H, E, I, top_k)
+    b = workspace.view(torch.uint8)
+    tk = T * top_k
+
+    def view(off, n, dt, shape):
+        return b[off:off + n * torch.tensor([], dtype=dt).element_size()].view(dt).view(*shape)
+
+    return dict(idx=view(lay.idx, tk, torch.int32, (T, top_k)),
+                gate=view(lay.gate, tk, torch.float32, (T, top_k)),
+                h=view(lay.h, tk * I, torch.bfloat16, (T, top_k, I)),
+                e=view(lay.e, tk * H, torch.float32, (T, top_k, H)))

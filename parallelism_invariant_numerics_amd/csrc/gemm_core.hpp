@@ -182,8 +182,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
 // voff are used).
 constexpr int kMaxDma = 4;
 struct Pipe {
-    __amdgpu_buffer_rsrc_t ra, rb;  // A tile rows, B tile rows
-    uint32_t voff[kMaxDma];         // this lane's byte offsets for its DMA rows
+    __amdgpu_buffer_rsrc_t ra, rb;  // A rows, B tile rows
+    uint32_t voffa[kMaxDma];        // this lane's byte offsets for its A and B DMA rows
+    uint32_t voffb[kMaxDma];
     uint32_t kbyte0;                // byte offset of the tile's first k (partition start)
 };
 
@@ -207,7 +208,8 @@ __device__ __forceinline__ Pipe make_pipe(const uint16_t *A_tile, int64_t rowsA,
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i) {
         const uint32_t r = C::kDma * 8 * w + 8 * i + (lane >> 3);
-        p.voff[i] = (uint32_t)((int64_t)r * K * 2) + c * 16;
+        p.voffa[i] = (uint32_t)((int64_t)r * K * 2) + c * 16;
+        p.voffb[i] = p.voffa[i];
     }
     p.kbyte0 = (uint32_t)(k0 * 2);
     return p;
@@ -222,11 +224,11 @@ __device__ __forceinline__ void stage_dma(const Pipe &p, char *lds, int st, int 
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(p.ra, (ISO_LDS void *)(dst + i * 8 * kRowBytes),
-                                                 16, p.voff[i], soff, 0, 0);
+                                                 16, p.voffa[i], soff, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            p.rb, (ISO_LDS void *)(dst + kBOffset + i * 8 * kRowBytes), 16, p.voff[i], soff, 0,
+            p.rb, (ISO_LDS void *)(dst + kBOffset + i * 8 * kRowBytes), 16, p.voffb[i], soff, 0,
             0);
 }
 

@@ -287,6 +287,122 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
     return launch_status(iso::launch_lmhead_finish(stats, target, tok, logprob, M, V, st));
 }
 
+namespace {
+
+struct MoeFull {
+    iso_moe_layout pub;
+    size_t counts, rows, tiles, ntiles;
+    int max_tiles;
+};
+
+iso_status moe_dims(int64_t T, int64_t H, int64_t E, int64_t I, int top_k)
+{
+    if (T < 0 || H < 1 || I < 1 || E < 1 || top_k < 1)
+        return ISO_ERR_ARG;
+    if (E > 1024 || top_k > 16 || top_k > E)
+        return ISO_ERR_SHAPE;
+    if (H % 64 != 0 || I % 64 != 0 || H > kMaxK || I > kMaxK)
+        return ISO_ERR_SHAPE;
+    if (T * top_k >= kMaxRows || T * H * 2 >= ((int64_t)1 << 32) ||
+        T * top_k * I * 2 >= ((int64_t)1 << 32) || I * H * 2 >= ((int64_t)1 << 32))
+        return ISO_ERR_SHAPE;
+    return ISO_OK;
+}
+
+MoeFull moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int top_k)
+{
+    MoeFull l;
+    const size_t tk = (size_t)T * top_k;
+    size_t o = 0;
+    l.pub.idx = o;
+    o += align_up(tk * 4);
+    l.pub.gate = o;
+    o += align_up(tk * 4);
+    l.pub.h = o;
+    o += align_up(tk * (size_t)I * 2);
+    l.pub.e = o;
+    o += align_up(tk * (size_t)H * 4);
+    l.counts = o;
+    o += align_up((size_t)E * 4);
+    l.rows = o;
+    o += align_up((size_t)E * (size_t)T * 4);
+    l.max_tiles = (int)(E + (tk + 127) / 128);
+    l.tiles = o;
+    o += align_up((size_t)l.max_tiles * 2 * 4);
+    l.ntiles = o;
+    o += 256;
+    l.pub.total = o;
+    return l;
+}
+
+}  // namespace
+
+iso_status iso_moe_layout_of(int64_t T, int64_t H, int64_t E, int64_t I, int top_k,
+                             iso_moe_layout *out)
+{
+    if (!out)
+        return ISO_ERR_ARG;
+    iso_status s = moe_dims(T, H, E, I, top_k);
+    if (s != ISO_OK)
+        return s;
+    *out = moe_layout(T, H, E, I, top_k).pub;
+    return ISO_OK;
+}
+
+size_t iso_moe_workspace(int64_t T, int64_t H, int64_t E, int64_t I, int top_k)
+{
+    if (moe_dims(T, H, E, I, top_k) != ISO_OK)
+        return (size_t)-1;
+    return moe_layout(T, H, E, I, top_k).pub.total;
+}
+
+iso_status iso_moe_combine(const iso_contract *gate_up, const iso_contract *down,
+                           const void *X, const float *router_logits, const void *Wg,
+                           const void *Wu, const void *Wd, float *Y, int64_t T, int64_t H,
+                           int64_t E, int64_t I, int top_k, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    iso_status s = check_contract(gate_up, 0);
+    if (s != ISO_OK)
+        return s;
+    if ((s = check_contract(down, 0)) != ISO_OK)
+        return s;
+    if ((s = moe_dims(T, H, E, I, top_k)) != ISO_OK)
+        return s;
+    if (H != (int64_t)gate_up->leaf_count * gate_up->leaf_size ||
+        I != (int64_t)down->leaf_count * down->leaf_size)
+        return ISO_ERR_SHAPE;
+    if (gate_up->leaf_count > (uint32_t)kMaxLeavesPerTile ||
+        down->leaf_count > (uint32_t)kMaxLeavesPerTile)
+        return ISO_ERR_SHAPE;
+    if (T == 0)
+        return ISO_OK;
+    if (!X || !router_logits || !Wg || !Wu || !Wd || !Y || !aligned16(X) || !aligned16(Wg) ||
+        !aligned16(Wu) || !aligned16(Wd) || !aligned16(Y))
+        return ISO_ERR_ARG;
+    const MoeFull l = moe_layout(T, H, E, I, top_k);
+    if (!workspace || workspace_bytes < l.pub.total || ((uintptr_t)workspace & 255u) != 0)
+        return ISO_ERR_WORKSPACE;
+
+    clear_stale_error();
+    char *ws = static_cast<char *>(workspace);
+    iso::MoeBuffers b;
+    b.idx = reinterpret_cast<int32_t *>(ws + l.pub.idx);
+    b.gate = reinterpret_cast<float *>(ws + l.pub.gate);
+    b.h = reinterpret_cast<uint16_t *>(ws + l.pub.h);
+    b.e = reinterpret_cast<float *>(ws + l.pub.e);
+    b.counts = reinterpret_cast<int32_t *>(ws + l.counts);
+    b.rows = reinterpret_cast<int32_t *>(ws + l.rows);
+    b.tiles = reinterpret_cast<int32_t *>(ws + l.tiles);
+    b.ntiles = reinterpret_cast<int32_t *>(ws + l.ntiles);
+    b.max_tiles = l.max_tiles;
+    return launch_status(iso::launch_moe(
+        static_cast<const uint16_t *>(X), router_logits, static_cast<const uint16_t *>(Wg),
+        static_cast<const uint16_t *>(Wu), static_cast<const uint16_t *>(Wd), Y, T, H, E, I,
+        top_k, (int)gate_up->leaf_count, (int)gate_up->leaf_size, (int)down->leaf_count,
+        (int)down->leaf_size, b, static_cast<hipStream_t>(stream)));
+}
+
 const char *iso_status_str(iso_status s)
 {
     switch (s) {

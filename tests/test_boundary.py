@@ -156,3 +156,29 @@ def test_lmhead_rejections_before_launch():
     assert _lm(c, wsb=need - 1) == 6
     assert _lm(c, M=0) == 0
     assert iso.lmhead_workspace(c, 8, 512, 2) >= need + 2 * 8 * 512 * 4
+
+
+def _moe(T=16, H=256, E=8, I=128, k=4, gu=(4, 64), dn=(2, 64), X=FAKE, ws=FAKE, wsb=1 << 40):
+    cg = iso.contract(*gu, 0)
+    cd = iso.contract(*dn, 0)
+    return iso.lib.iso_moe_combine(ctypes.byref(cg), ctypes.byref(cd), X, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, T, H, E, I, k, ws, wsb, None)
+
+
+def test_moe_rejections_before_launch():
+    assert _moe(E=0) == 1
+    assert _moe(E=1025, k=4) == 2
+    assert _moe(k=17, E=32) == 2
+    assert _moe(k=9, E=8) == 2
+    assert _moe(k=0) == 1
+    assert _moe(gu=(8, 64)) == 2          # H != L * m
+    assert _moe(dn=(4, 64)) == 2          # I != L * m
+    assert _moe(H=2048, gu=(32, 64)) == 2  # too many leaves for the expert kernels
+    assert _moe(T=0) == 0
+    assert _moe(X=None) == 1
+    need = iso.moe_workspace(16, 256, 8, 128, 4)
+    assert _moe(wsb=need - 1) == 6
+    assert _moe(ws=FAKE + 16) == 6        # workspace must be 256-byte aligned
+    lay = iso.moe_layout(16, 256, 8, 128, 4)
+    assert lay.idx < lay.gate < lay.h < lay.e < lay.total == need
+    assert lay.e - lay.h >= 16 * 4 * 128 * 2 and lay.total - lay.e >= 16 * 4 * 256 * 4

@@ -1,0 +1,155 @@
+"""GPU parity of iso_moe_combine with the oracle, stage by stage, and the
+bit-identity of every token's output across token orderings.
+
+Stages (the workspace keeps each stage's output):
+  route    expert ids equal the oracle's exactly; gates within 4e-7 relative;
+  gate/up  bf16 h equals the oracle's activation rounded to bf16, or differs
+           by one bf16 step where the activation lies within its tolerance of
+           a rounding midpoint (the decision is taken in FP32 on both sides,
+           from G and U that agree to 1e-5 * sum|x w|);
+  down     e = h Wd with the GPU's own h, within 1e-5 * sum|h w|;
+  combine  y within 1e-5 * sum_k |g_k e_k| of the oracle's combine of the
+           GPU's e with the oracle's gates.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import dev, host, note, torch
+from iso_synth import bf16_bits_to_f32, make_config, normal_bf16, normal_f32
+
+pytestmark = pytest.mark.gpu
+
+iso = pytest.importorskip("parallelism_invariant_numerics_amd")
+
+
+def _run(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, dW=None):
+    t = torch()
+    T, H = X.shape
+    E, I, _ = Wg.shape
+    cg = iso.contract(Lgu, H // Lgu, 0)
+    cd = iso.contract(Ldn, I // Ldn, 0)
+    dW = dW or (dev(Wg), dev(Wu), dev(Wd))
+    ws = t.empty(iso.moe_workspace(T, H, E, I, k), dtype=t.uint8, device="cuda")
+    y = iso.moe_combine(dev(X), t.from_numpy(lg).to("cuda"), *dW, k, cg, cd, workspace=ws)
+    t.cuda.synchronize()
+    st = iso.moe_stages(ws, T, H, E, I, k)
+    return host(y), {n: host(v) for n, v in st.items()}
+
+
+def _check_stages(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, y, st, what):
+    T, H = X.shape
+    E, I, _ = Wg.shape
+    idx, gate = oracle.moe_route(lg, k)
+    assert np.array_equal(st["idx"], idx), what
+    assert np.allclose(st["gate"], gate, rtol=4e-7, atol=0), what
+    # gate/up: oracle G, U per expert on the GPU's routing
+    x = bf16_bits_to_f32(X).astype(np.float64)
+    act = np.zeros((T, k, I))
+    tol = np.zeros((T, k, I))
+    for e in np.unique(idx):
+        tt, ss = np.nonzero(idx == e)
+        G = oracle.gemm(X[tt], Wg[e], Lgu).astype(np.float64)
+        U = oracle.gemm(X[tt], Wu[e], Lgu).astype(np.float64)
+        adg = np.abs(x[tt]) @ np.abs(bf16_bits_to_f32(Wg[e]).astype(np.float64)).T
+        adu = np.abs(x[tt]) @ np.abs(bf16_bits_to_f32(Wu[e]).astype(np.float64)).T
+        sig = 1.0 / (1.0 + np.exp(-G))
+        silu = G * sig
+        dsilu = np.abs(sig * (1.0 + G * (1.0 - sig)))
+        act[tt, ss] = silu * U
+        tol[tt, ss] = (dsilu * np.abs(U) * 1e-5 * adg + np.abs(silu) * 1e-5 * adu
+                       + 8 * 2.0 ** -24 * np.abs(silu * U))
+    h = bf16_bits_to_f32(st["h"]).astype(np.float64)
+    half_ulp = np.abs(act) * 2.0 ** -8 + 1e-30  # one bf16 rounding step, bounds the half-ulp too
+    assert np.all(np.abs(h - act) <= half_ulp + tol), what
+    # down with the GPU's own h
+    e_or = oracle.moe_down(st["h"], Wd, st["idx"], Ldn).astype(np.float64)
+    hh = np.abs(h)
+    for slot in range(k):
+        for tt in range(T):
+            ad = hh[tt, slot] @ np.abs(bf16_bits_to_f32(Wd[st["idx"][tt, slot]]).astype(np.float64)).T
+            err = np.abs(st["e"][tt, slot] - e_or[tt, slot])
+            assert np.all(err <= 1e-5 * ad), (what, tt, slot)
+    # combine with the oracle's gates and the GPU's e
+    y_or = oracle.moe_combine(gate, st["e"])
+    scale = np.einsum("tk,tkh->th", np.abs(gate), np.abs(st["e"].astype(np.float64)))
+    assert np.all(np.abs(y - y_or) <= 1e-5 * scale + 1e-30), what
+
+
+@pytest.mark.parametrize("T,H,E,I,k,Lgu,Ldn", [(64, 256, 8, 128, 4, 4, 2), (37, 512, 16, 64, 2, 2, 1),
+                                               (130, 256, 64, 128, 8, 4, 2), (5, 128, 3, 192, 3, 1, 1)])
+def test_small_parity_by_stage(T, H, E, I, k, Lgu, Ldn):
+    X = normal_bf16(T + 1, (T, H), 1.0)
+    lg = normal_f32(T + 2, (T, E))
+    Wg = normal_bf16(T + 3, (E, I, H), 0.05)
+    Wu = normal_bf16(T + 4, (E, I, H), 0.05)
+    Wd = normal_bf16(T + 5, (E, H, I), 0.05)
+    note(f"moe small T={T} H={H} E={E} I={I} k={k}")
+    y, st = _run(X, lg, Wg, Wu, Wd, k, Lgu, Ldn)
+    _check_stages(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, y, st, f"T={T}")
+
+
+def test_top1_and_identical_experts():
+    T, H, E, I = 20, 256, 4, 128
+    X = normal_bf16(1, (T, H), 1.0)
+    lg = normal_f32(2, (T, E))
+    Wg = np.repeat(normal_bf16(3, (1, I, H), 0.05), E, axis=0)
+    Wu = np.repeat(normal_bf16(4, (1, I, H), 0.05), E, axis=0)
+    Wd = np.repeat(normal_bf16(5, (1, H, I), 0.05), E, axis=0)
+    note("moe top-1")
+    y1, st1 = _run(X, lg, Wg, Wu, Wd, 1, 4, 2)
+    assert np.all(st1["gate"] == 1.0)
+    assert np.array_equal(y1.view(np.uint32), st1["e"][:, 0].view(np.uint32))
+    note("moe identical experts")
+    y4, st4 = _run(X, lg, Wg, Wu, Wd, 4, 4, 2)
+    for s in range(1, 4):  # every expert computes the same bits for a token
+        assert np.array_equal(st4["e"][:, s].view(np.uint32), st4["e"][:, 0].view(np.uint32))
+    assert np.allclose(y4, st4["e"][:, 0], rtol=4 * 2.0 ** -23, atol=1e-30)
+
+
+def test_token_orderings_bitwise():
+    T, H, E, I, k = 300, 512, 32, 128, 8
+    X = normal_bf16(11, (T, H), 1.0)
+    lg = normal_f32(12, (T, E))
+    Wg = normal_bf16(13, (E, I, H), 0.05)
+    Wu = normal_bf16(14, (E, I, H), 0.05)
+    Wd = normal_bf16(15, (E, H, I), 0.05)
+    dW = (dev(Wg), dev(Wu), dev(Wd))
+    note("moe orderings: identity")
+    y0, _ = _run(X, lg, Wg, Wu, Wd, k, 4, 2, dW)
+    rng = np.random.default_rng(16)
+    perms = [np.arange(T)[::-1].copy()] + [rng.permutation(T) for _ in range(3)]
+    for i, perm in enumerate(perms):
+        note(f"moe orderings: permutation {i}")
+        yp, _ = _run(X[perm], lg[perm], Wg, Wu, Wd, k, 4, 2, dW)
+        assert np.array_equal(yp.view(np.uint32), y0[perm].view(np.uint32)), i
+    note("moe orderings: sub-batch")
+    sub = rng.choice(T, 77, replace=False)
+    ys, _ = _run(X[sub], lg[sub], Wg, Wu, Wd, k, 4, 2, dW)
+    assert np.array_equal(ys.view(np.uint32), y0[sub].view(np.uint32))
+
+
+def test_moe_full_size():
+    cfg = make_config("moe")
+    T, H, E, I, k = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["top_k"]
+    Lgu, Ldn = cfg["leaves_gate_up"], cfg["leaves_down"]
+    dW = (dev(cfg["Wg"]), dev(cfg["Wu"]), dev(cfg["Wd"]))
+    note("moe full size 4096 tokens, 128 experts, top-8")
+    y, st = _run(cfg["X"], cfg["logits"], cfg["Wg"], cfg["Wu"], cfg["Wd"], k, Lgu, Ldn, dW)
+    idx, gate = oracle.moe_route(cfg["logits"], k)
+    assert np.array_equal(st["idx"], idx)
+    assert np.allclose(st["gate"], gate, rtol=4e-7, atol=0)
+    assert np.all(np.isfinite(y))
+    # sampled tokens through every stage (a token's numbers depend only on itself)
+    sel = np.array([0, 1, 2047, 4095, 1234, 3333])
+    sub = {n: v[sel] for n, v in st.items()}
+    _check_stages(cfg["X"][sel], cfg["logits"][sel], cfg["Wg"], cfg["Wu"], cfg["Wd"], k, Lgu, Ldn,
+                  y[sel], sub, "full-size sample")
+    note("moe full size, reversed order")
+    rev = np.arange(T)[::-1].copy()
+    yr, _ = _run(cfg["X"][rev], cfg["logits"][rev], cfg["Wg"], cfg["Wu"], cfg["Wd"], k, Lgu, Ldn, dW)
+    assert np.array_equal(yr.view(np.uint32), y[rev].view(np.uint32))
+    note("moe full size, first 1024 tokens")
+    y1k, _ = _run(cfg["X"][:1024], cfg["logits"][:1024], cfg["Wg"], cfg["Wu"], cfg["Wd"], k, Lgu,
+                  Ldn, dW)
+    assert np.array_equal(y1k.view(np.uint32), y[:1024].view(np.uint32))
