@@ -40,9 +40,10 @@ def _args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--quick", action="store_true", help="headline GEMM only (for profiling)")
+    p.add_argument("--quick", action="store_true",
+                   help="headline GEMM launches only (for rocprofv3 runs)")
     p.add_argument("--calibrate-copy", action="store_true",
-                   help="run one 1 GiB device copy first (HBM counter calibration)")
+                   help="first run one plain copy kernel over 256 MiB (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -128,9 +129,10 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # an elementwise kernel that reads 256 MiB and writes 256 MiB
+        src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -165,11 +167,14 @@ def main():
                    "M": M, "N": N, "K": K, "leaves": L, "leaf_size": K // L, "partitions": 1},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(src_hash), "kernel": "gemm_leaf_kernel<3>",
+                     "traffic": _traffic(src_hash), "kernel": "gemm_leaf_kernel<CfgWide, 3>",
                      "kernel_ms": round(kern_ms, 5), "algorithmic_flop": flop,
                      "source_hash": src_hash},
     }
     extra = {}
+    if args.quick:
+        print(json.dumps(line), flush=True)
+        return
 
     # ---------------- cost of invariance on the same shape
     outb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")

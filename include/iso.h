@@ -145,7 +145,7 @@ size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int parti
  * `partitions` P emulates P tensor-parallel ranks on this GPU: partition p
  * computes its subtree root into the workspace and a combine kernel applies
  * the top log2(P) levels.  Every P allowed by the claim gives the same bits.
- * Limits: M, N < 2^23, K <= 2^22.
+ * Limits: M, N < 2^23 and (M/128)(N/128) < 2^28 tiles, K <= 2^22.
  */
 iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *C,
                     uint32_t out_dtype, int64_t M, int64_t N, int64_t K, int partitions,

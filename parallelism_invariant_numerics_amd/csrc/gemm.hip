@@ -16,6 +16,8 @@ namespace iso {
 
 enum OutMode : int { kOutF32 = 0, kOutBF16 = 1, kOutWorkspace = 2 };
 
+constexpr int kTileGroup = 8;  // tile rows per group of the XCD-aware order
+
 struct GemmParams {
     const uint16_t *A;
     const uint16_t *Wt;
@@ -30,9 +32,14 @@ template <class C, int LOG>
 __global__ __launch_bounds__(C::kThreads, 2) void gemm_leaf_kernel(GemmParams p)
 {
     __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-    const int part = blockIdx.z;
+    const int tm = static_cast<int>((p.M + BM - 1) / BM);
+    const int tn = static_cast<int>((p.N + BN - 1) / BN);
+    const int ntile = tm * tn;
+    const int part = blockIdx.x / ntile;  // partition-major; tiles of a partition together
+    int mt, nt;
+    xcd_tile(blockIdx.x % ntile + 0, ntile, tm, tn, kTileGroup, mt, nt);
+    const int64_t m0 = static_cast<int64_t>(mt) * BM;
+    const int64_t n0 = static_cast<int64_t>(nt) * BN;
 
     const Pipe pipe = make_pipe<C>(p.A + m0 * p.K, p.M - m0, p.Wt + n0 * p.K, p.N - n0, p.K,
                                       part * p.k_per_part);
@@ -90,8 +97,8 @@ template <int LOG>
 static hipError_t launch_leaf(const GemmParams &p, int parts, hipStream_t stream)
 {
     using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
-    dim3 grid(static_cast<unsigned>((p.N + BN - 1) / BN), static_cast<unsigned>((p.M + BM - 1) / BM),
-              static_cast<unsigned>(parts));
+    const int64_t tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+    dim3 grid(static_cast<unsigned>(tiles * parts));
     hipLaunchKernelGGL((gemm_leaf_kernel<C, LOG>), grid, dim3(C::kThreads), 0, stream, p);
     return hipGetLastError();
 }

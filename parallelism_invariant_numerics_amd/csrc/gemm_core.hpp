@@ -358,6 +358,29 @@ __device__ __forceinline__ int tile_col(int lane, int wc, int j)
     return wc * (BN / C::WC) + j * 16 + (lane & 15);
 }
 
+// XCD-aware tile order.  Workgroups are dispatched round-robin over the
+// 8 XCDs (workgroup b runs on XCD b % 8), and each XCD has its own L2.  The
+// linear workgroup id is renumbered so that each XCD walks one contiguous
+// stretch of a grouped tile order (G tile rows at a time, rows fastest),
+// i.e. a compact block of output tiles whose A rows and B columns its L2
+// shares.  Returns the tile's (row block, column block) in a tm x tn grid.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tm, int tn, int group,
+                                         int &mt, int &nt)
+{
+    const int xcd = bid % kXcds;
+    const int per = nblocks / kXcds;
+    const int extra = nblocks % kXcds;
+    const int t = xcd * per + (xcd < extra ? xcd : extra) + bid / kXcds;
+    const int gsz_full = group * tn;
+    const int g = t / gsz_full;
+    const int first = g * group;
+    const int rows = tm - first < group ? tm - first : group;
+    const int r = t % gsz_full;
+    mt = first + r % rows;
+    nt = r / rows;
+}
+
 // Fixed tree over P partition roots (P = 1, 2, 4, 8), lower index left.
 template <int P>
 __device__ __forceinline__ float fold_roots(const float (&r)[P])

@@ -82,9 +82,14 @@ iso_status check_gemm_shape(const iso_contract *c, int64_t M, int64_t N, int64_t
     return ISO_OK;
 }
 
+// The tile grid is one-dimensional: (M/128) * (N/128) * 8 partitions must
+// stay below 2^31 workgroups.
 iso_status check_gemm_dims(int64_t M, int64_t N)
 {
-    return (M >= kMaxDim || N >= kMaxDim) ? ISO_ERR_SHAPE : ISO_OK;
+    if (M >= kMaxDim || N >= kMaxDim)
+        return ISO_ERR_SHAPE;
+    return ((M + 127) / 128) * ((N + 127) / 128) * 8 < ((int64_t)1 << 31) ? ISO_OK
+                                                                          : ISO_ERR_SHAPE;
 }
 
 }  // namespace
@@ -261,6 +266,8 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
     if ((s = check_gemm_shape(c, M, V, K)) != ISO_OK)
         return s;
     if (V < 1 || V > kMaxVocab)
+        return ISO_ERR_SHAPE;
+    if (((M + 127) / 128) * ((V + 127) / 128) >= ((int64_t)1 << 31))
         return ISO_ERR_SHAPE;
     if ((s = iso_check_partitions(c, partitions)) != ISO_OK)
         return s;

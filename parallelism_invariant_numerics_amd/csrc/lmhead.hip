@@ -173,8 +173,12 @@ template <class C, int LOG>
 __global__ __launch_bounds__(C::kThreads, 2) void lmhead_fused_kernel(LmArgs a)
 {
     __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+    const int tm = static_cast<int>((a.M + BM - 1) / BM);
+    const int tn = static_cast<int>(a.nchunk);
+    int mt, nt;
+    xcd_tile(blockIdx.x, tm * tn, tm, tn, 8, mt, nt);
+    const int64_t m0 = static_cast<int64_t>(mt) * BM;
+    const int64_t n0 = static_cast<int64_t>(nt) * BN;
 
     const Pipe pipe =
         make_pipe<C>(a.H + m0 * a.K, a.M - m0, a.Wvt + n0 * a.K, a.V - n0, a.K, 0);
@@ -281,7 +285,7 @@ template <int LOG>
 static hipError_t launch_fused(const LmArgs &a, hipStream_t stream)
 {
     using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
-    dim3 grid(static_cast<unsigned>((a.M + BM - 1) / BM), static_cast<unsigned>(a.nchunk));
+    dim3 grid(static_cast<unsigned>(((a.M + BM - 1) / BM) * a.nchunk));
     hipLaunchKernelGGL((lmhead_fused_kernel<C, LOG>), grid, dim3(C::kThreads), 0, stream, a);
     return hipGetLastError();
 }
