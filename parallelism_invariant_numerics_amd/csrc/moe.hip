@@ -143,31 +143,41 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *logits, int
 // --------------------------------------------------------------- bucket
 
 // Expert e = blockIdx.x gathers the entries i = t * top_k + slot with
-// idx[i] == e, in increasing i, into rows[e][0 .. count).
+// idx[i] == e, in increasing i, into rows[e][0 .. count).  Each pass covers
+// 2048 entries: thread j owns entries [8j, 8j + 8) of the pass; an exclusive
+// scan of the per-thread match counts gives every match its ordered slot.
 __global__ __launch_bounds__(256) void moe_bucket_kernel(const int32_t *idx, int32_t *rows,
                                                          int32_t *counts, int64_t n_entries,
                                                          int64_t T)
 {
-    __shared__ int wave_tot[4];
+    __shared__ int scan[256];
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
     int32_t *dst = rows + static_cast<int64_t>(e) * T;
     int count = 0;
-    for (int64_t base = 0; base < n_entries; base += 256) {
-        const int64_t i = base + tid;
-        const bool match = i < n_entries && idx[i] == e;
-        const uint64_t bal = __ballot(match);
-        const int before = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0)
-            wave_tot[wave] = __popcll(bal);
+    for (int64_t base = 0; base < n_entries; base += 2048) {
+        const int64_t i0 = base + static_cast<int64_t>(tid) * 8;
+        unsigned mask = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (i0 + j < n_entries && idx[i0 + j] == e)
+                mask |= 1u << j;
+        const int mine = __popc(mask);
+        scan[tid] = mine;
         __syncthreads();
-        int off = count;
-        for (int w = 0; w < wave; ++w)
-            off += wave_tot[w];
-        if (match)
-            dst[off + before] = static_cast<int32_t>(i);
-        count += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+        // inclusive Hillis-Steele scan over the 256 counts
+        for (int d = 1; d < 256; d <<= 1) {
+            const int add = tid >= d ? scan[tid - d] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        int pos = count + scan[tid] - mine;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (mask & (1u << j))
+                dst[pos++] = static_cast<int32_t>(i0 + j);
+        count += scan[255];
         __syncthreads();
     }
     if (tid == 0)
@@ -176,18 +186,30 @@ __global__ __launch_bounds__(256) void moe_bucket_kernel(const int32_t *idx, int
 
 // ------------------------------------------------------------------ plan
 
-__global__ void moe_plan_kernel(const int32_t *counts, int32_t *tiles, int32_t *ntiles, int E)
+// Work list of (expert, first row) tiles in expert order: thread e (E <=
+// 1024 threads) scans the per-expert tile counts and writes its own tiles.
+__global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *counts, int32_t *tiles,
+                                                        int32_t *ntiles, int E)
 {
-    if (threadIdx.x != 0 || blockIdx.x != 0)
-        return;
-    int n = 0;
-    for (int e = 0; e < E; ++e)
-        for (int m0 = 0; m0 < counts[e]; m0 += BM) {
-            tiles[2 * n] = e;
-            tiles[2 * n + 1] = m0;
-            ++n;
-        }
-    *ntiles = n;
+    __shared__ int scan[1024];
+    const int e = threadIdx.x;
+    const int c = e < E ? counts[e] : 0;
+    const int mine = (c + BM - 1) / BM;
+    scan[e] = mine;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int add = e >= d ? scan[e - d] : 0;
+        __syncthreads();
+        scan[e] += add;
+        __syncthreads();
+    }
+    int n = scan[e] - mine;
+    for (int m0 = 0; m0 < c; m0 += BM, ++n) {
+        tiles[2 * n] = e;
+        tiles[2 * n + 1] = m0;
+    }
+    if (e == 1023)
+        *ntiles = scan[1023];
 }
 
 // --------------------------------------------------------------- experts
@@ -250,7 +272,15 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(MoeGemmArgs 
     constexpr int TN = GATE_UP ? kGuCols : BN;  // output columns per tile
     const int ntn = static_cast<int>((a.N + TN - 1) / TN);
     const int total = __builtin_amdgcn_readfirstlane(*a.ntiles) * ntn;
-    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    // XCD-aware work split: the workgroups on XCD x (blockIdx % 8 == x) take
+    // the contiguous task range [x per, (x+1) per), so the tasks running
+    // together on one L2 share an expert's weights and a tile's rows.  The
+    // grid is a multiple of 8, so every task is taken exactly once.
+    const int xcd = blockIdx.x % kXcds;
+    const int slots = gridDim.x / kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
+    for (int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds; w < end; w += slots) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores drained
         const int tile = w / ntn;
         const int64_t n0 = static_cast<int64_t>(w % ntn) * TN;
@@ -367,6 +397,7 @@ static void launch_expert(const MoeGemmArgs &a, hipStream_t stream)
 {
     using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
     const unsigned grid = LOG <= 1 ? 512 : 256;  // resident workgroups on 256 CUs
+    static_assert(kXcds == 8, "the task split assumes a grid that is a multiple of 8");
     hipLaunchKernelGGL((moe_expert_kernel<C, LOG, GU>), dim3(grid), dim3(C::kThreads), 0, stream,
                        a);
 }
@@ -404,8 +435,8 @@ hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg
         return err;
     hipLaunchKernelGGL(moe_bucket_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream,
                        b.idx, b.rows, b.counts, T * top_k, T);
-    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(64), 0, stream, b.counts, b.tiles, b.ntiles,
-                       (int)E);
+    hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, stream, b.counts, b.tiles,
+                       b.ntiles, (int)E);
     if ((err = hipGetLastError()) != hipSuccess)
         return err;
 
