@@ -52,12 +52,25 @@ def _dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
+def _settle(fn, seconds=0.3):
+    """Run fn back to back for about `seconds` of wall time, untimed.  The
+    GPU raises its clocks only after some tens of milliseconds of sustained
+    load; a few warmup steps of a 50 us kernel would time the ramp instead of
+    the steady state."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _time_events(fn, steps, stream):
     """Average duration (ms) of one fn() call: HIP events on `stream` around
     `steps` back-to-back calls (the launches queue up, so host-side call
     overhead does not appear as idle GPU time between them)."""
     import torch
-    fn()
+    _settle(fn, 0.2)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -143,6 +156,7 @@ def main():
     c = iso.contract(L, K // L, 0)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     step = lambda: iso.gemm(A, W, c, out=out, out_dtype=iso.BF16)
+    _settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -46,29 +46,16 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_leaf_kernel(GemmParams p)
     Acc<C> root;
     leaf_tree_mainloop<C, LOG>(pipe, p.stages_per_leaf, lds, root);
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wr = wave / C::WC, wc = wave % C::WC;
-#pragma unroll
-    for (int i = 0; i < C::IB; ++i)
-#pragma unroll
-        for (int j = 0; j < C::JB; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + tile_row<C>(lane, wr, i, r);
-                const int64_t col = n0 + tile_col<C>(lane, wc, j);
-                if (row >= p.M || col >= p.N)
-                    continue;
-                const float v = root.v[i][j][r];
-                if (p.mode == kOutF32) {
-                    static_cast<float *>(p.out)[row * p.N + col] = v;
-                } else if (p.mode == kOutBF16) {
-                    static_cast<uint16_t *>(p.out)[row * p.N + col] = f32_to_bf16_rne(v);
-                } else {
-                    static_cast<float *>(p.out)[(static_cast<int64_t>(part) * p.M + row) * p.N +
-                                                col] = v;
-                }
-            }
+    if (p.mode == kOutWorkspace) {
+        float *ws = static_cast<float *>(p.out) + (static_cast<int64_t>(part) * p.M + m0) * p.N + n0;
+        store_tile<C>(root, lds, ws, p.N, p.M - m0, p.N - n0, false);
+    } else if (p.mode == kOutBF16) {
+        store_tile<C>(root, lds, static_cast<uint16_t *>(p.out) + m0 * p.N + n0, p.N, p.M - m0,
+                      p.N - n0, true);
+    } else {
+        store_tile<C>(root, lds, static_cast<float *>(p.out) + m0 * p.N + n0, p.N, p.M - m0,
+                      p.N - n0, false);
+    }
 }
 
 // Top log2(P) tree levels over the partition roots ws[p][M][N].

@@ -358,6 +358,116 @@ __device__ __forceinline__ int tile_col(int lane, int wc, int j)
     return wc * (BN / C::WC) + j * 16 + (lane & 15);
 }
 
+// ------------------------------------------------------------------ epilogue
+
+// A tile's FP32 roots staged in LDS so that the global stores can be whole
+// 16-byte vectors instead of one element per lane; the values pass unchanged.
+// Layout: 128 rows of 512 bytes; the 16-byte chunk c of row r sits at chunk
+// c ^ (4 ((r >> 2) & 3)), which puts the four row groups of one MFMA output
+// register on disjoint banks.  `lds` must hold 64 KiB that no wave still
+// reads (the stage ring after leaf_tree_mainloop returns); the function ends
+// with a workgroup barrier.
+template <class C>
+__device__ __forceinline__ const float *stage_tile(const Acc<C> &root, char *lds)
+{
+    static_assert(C::kLdsBytes >= BM * BN * 4, "the stage ring must hold the FP32 tile");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wr = wave / C::WC, wc = wave % C::WC;
+    float *stage = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::JB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = tile_row<C>(lane, wr, i, r);
+                const int col = tile_col<C>(lane, wc, j);
+                const int chunk = (col >> 2) ^ (((row >> 2) & 3) << 2);
+                stage[row * 128 + chunk * 4 + (col & 3)] = root.v[i][j][r];
+            }
+    __syncthreads();
+    return stage;
+}
+
+// Columns 4c .. 4c+3 of staged row `row`.
+__device__ __forceinline__ f32x4 staged_chunk(const float *stage, int row, int c)
+{
+    return *reinterpret_cast<const f32x4 *>(stage + row * 128 +
+                                            ((c ^ (((row >> 2) & 3) << 2)) << 2));
+}
+
+// Store 8 bf16 (rounded to nearest even) or 4 FP32 values at dst, whole when
+// `vec` (16-byte aligned and all in range), else only the first `n`.
+__device__ __forceinline__ void store8_bf16(uint16_t *dst, const float (&v)[8], bool vec, int n)
+{
+    if (vec) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = static_cast<uint32_t>(f32_to_bf16_rne(v[2 * e])) |
+                   (static_cast<uint32_t>(f32_to_bf16_rne(v[2 * e + 1])) << 16);
+        *reinterpret_cast<u32x4 *>(dst) = w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < n)
+                dst[e] = f32_to_bf16_rne(v[e]);
+    }
+}
+__device__ __forceinline__ void store4_f32(float *dst, const f32x4 &v, bool vec, int n)
+{
+    if (vec) {
+        *reinterpret_cast<f32x4 *>(dst) = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n)
+                dst[e] = v[e];
+    }
+}
+
+// Write a tile's roots to a row-major output: FP32 unchanged or bf16 rounded
+// to nearest even.  Tile row r goes to output row r, or to row_map[r] when
+// `row_map` is given.
+//   out       tile column 0 of output row 0
+//   ld        output row stride in elements
+//   rows, cols  rows / columns of the tile inside the matrix (clipped to 128)
+template <class C>
+__device__ __forceinline__ void store_tile(const Acc<C> &root, char *lds, void *out, int64_t ld,
+                                           int64_t rows, int64_t cols, bool bf16_out,
+                                           const int32_t *row_map = nullptr)
+{
+    const float *stage = stage_tile<C>(root, lds);
+    const int rmax = rows < BM ? static_cast<int>(rows) : BM;
+    const int cmax = cols < BN ? static_cast<int>(cols) : BN;
+    if (bf16_out) {
+        uint16_t *o = static_cast<uint16_t *>(out);
+        const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (ld % 8 == 0);
+        for (int u = threadIdx.x; u < BM * 16; u += C::kThreads) {
+            const int row = u >> 4, q = u & 15;
+            if (row >= rmax)
+                break;
+            const f32x4 lo = staged_chunk(stage, row, 2 * q);
+            const f32x4 hi = staged_chunk(stage, row, 2 * q + 1);
+            const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int64_t orow = row_map ? row_map[row] : row;
+            store8_bf16(o + orow * ld + 8 * q, v, al && 8 * q + 8 <= cmax, cmax - 8 * q);
+        }
+    } else {
+        float *o = static_cast<float *>(out);
+        const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (ld % 4 == 0);
+        for (int u = threadIdx.x; u < BM * 32; u += C::kThreads) {
+            const int row = u >> 5, q = u & 31;
+            if (row >= rmax)
+                break;
+            const int64_t orow = row_map ? row_map[row] : row;
+            store4_f32(o + orow * ld + 4 * q, staged_chunk(stage, row, q), al && 4 * q + 4 <= cmax,
+                       cmax - 4 * q);
+        }
+    }
+}
+
 // XCD-aware tile order.  Workgroups are dispatched round-robin over the
 // 8 XCDs (workgroup b runs on XCD b % 8), and each XCD has its own L2.  The
 // linear workgroup id is renumbered so that each XCD walks one contiguous

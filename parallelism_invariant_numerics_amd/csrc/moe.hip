@@ -307,61 +307,37 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(MoeGemmArgs 
         leaf_tree_mainloop<C, LOG>(p, a.stages_per_leaf, lds, r0);
 
         if constexpr (GATE_UP) {
-            float *ul = reinterpret_cast<float *>(lds);  // U of the tile: [128][64]
-            if (wc >= C::WC / 2) {
+            // h = bf16(silu(G) * U), G in tile columns 0..63, U in 64..127.
+            const float *stage = stage_tile<C>(r0, lds);
+            const float kLog2e = 1.44269504088896340736f;
+            uint16_t *o = static_cast<uint16_t *>(a.out) + n0;
+            const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (a.N % 8 == 0);
+            const int cmax = a.N - n0 < kGuCols ? static_cast<int>(a.N - n0) : kGuCols;
+            for (int u = threadIdx.x; u < BM * (kGuCols / 8); u += C::kThreads) {
+                const int row = u >> 3, q = u & 7;
+                if (row >= nvalid)
+                    break;
+                const f32x4 g0 = staged_chunk(stage, row, 2 * q);
+                const f32x4 g1 = staged_chunk(stage, row, 2 * q + 1);
+                const f32x4 u0 = staged_chunk(stage, row, kGuCols / 4 + 2 * q);
+                const f32x4 u1 = staged_chunk(stage, row, kGuCols / 4 + 2 * q + 1);
+                const float gs[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+                const float us[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                float v[8];
 #pragma unroll
-                for (int i = 0; i < C::IB; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::JB; ++j)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            ul[tile_row<C>(lane, wr, i, r) * kGuCols +
-                               (tile_col<C>(lane, wc, j) - kGuCols)] = r0.v[i][j][r];
-            }
-            __syncthreads();
-            if (wc < C::WC / 2) {
-                const float kLog2e = 1.44269504088896340736f;
-#pragma unroll
-                for (int i = 0; i < C::IB; ++i)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int rt = tile_row<C>(lane, wr, i, r);
-                        if (rt >= nvalid)
-                            continue;
-                        const int64_t dst = rows_e[m0 + rt];
-#pragma unroll
-                        for (int j = 0; j < C::JB; ++j) {
-                            const int cc = tile_col<C>(lane, wc, j);
-                            if (n0 + cc >= a.N)
-                                continue;
-                            const float g = r0.v[i][j][r];
-                            const float u = ul[rt * kGuCols + cc];
-                            const float ex = __builtin_amdgcn_exp2f(-g * kLog2e);
-                            const float sg = g / (1.0f + ex);
-                            const float v = sg * u;
-                            static_cast<uint16_t *>(a.out)[dst * a.N + n0 + cc] =
-                                f32_to_bf16_rne(v);
-                        }
-                    }
-            }
-            __syncthreads();  // the next tile's loads overwrite the LDS
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::IB; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int rt = tile_row<C>(lane, wr, i, r);
-                    if (rt >= nvalid)
-                        continue;
-                    const int64_t dst = rows_e[m0 + rt];
-#pragma unroll
-                    for (int j = 0; j < C::JB; ++j) {
-                        const int64_t col = n0 + tile_col<C>(lane, wc, j);
-                        if (col < a.N)
-                            static_cast<float *>(a.out)[dst * a.N + col] = r0.v[i][j][r];
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    const float ex = __builtin_amdgcn_exp2f(-gs[e] * kLog2e);
+                    const float sg = gs[e] / (1.0f + ex);
+                    v[e] = sg * us[e];
                 }
+                const int64_t dst = rows_e[m0 + row];
+                store8_bf16(o + dst * a.N + 8 * q, v, al && 8 * q + 8 <= cmax, cmax - 8 * q);
+            }
+        } else {
+            store_tile<C>(r0, lds, static_cast<float *>(a.out) + n0, a.N, nvalid, a.N - n0, false,
+                          rows_e + m0);
         }
+        __syncthreads();  // the next tile's loads overwrite the LDS
     }
 }
 
