@@ -68,4 +68,34 @@ __device__ __forceinline__ float shfl_xor(float v, int mask)
     return __shfl_xor(v, mask, kWave);
 }
 
+// Butterflies over the 16 lanes of a DPP row with the partners (l, l^1),
+// (l, l^2), (l, l^4), (l, l^8), on DPP moves instead of LDS permutes.  The
+// first two steps use exact xor patterns (quad_perm [1,0,3,2], [2,3,0,1]);
+// after them every quad holds one value, so the 8-lane half mirror and the
+// 16-lane mirror read the same partner values as xor 4 and xor 8.  Every
+// lane ends with the same result, and a sum is the balanced tree over the 16
+// lanes in index order (IEEE addition is commutative, so a + b in one lane
+// and b + a in its partner agree).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row16_sum(float e)
+{
+    e = e + dpp_mov<0xB1>(e);   // quad_perm [1,0,3,2]: l ^ 1
+    e = e + dpp_mov<0x4E>(e);   // quad_perm [2,3,0,1]: l ^ 2
+    e = e + dpp_mov<0x141>(e);  // row_half_mirror: the other quad of the 8
+    e = e + dpp_mov<0x140>(e);  // row_mirror: the other 8 of the 16
+    return e;
+}
+__device__ __forceinline__ float row16_max(float m)
+{
+    m = fmaxf(m, dpp_mov<0xB1>(m));
+    m = fmaxf(m, dpp_mov<0x4E>(m));
+    m = fmaxf(m, dpp_mov<0x141>(m));
+    m = fmaxf(m, dpp_mov<0x140>(m));
+    return m;
+}
+
 }  // namespace iso

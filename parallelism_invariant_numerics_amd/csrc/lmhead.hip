@@ -64,9 +64,12 @@ __device__ __forceinline__ float tree_waves(const float *red, int rt)
         return red[rt] + red[128 + rt];
 }
 
+// `tok_s` holds the tile rows' sampled token ids in LDS (written before the
+// first barrier below, by any thread).
 template <class C>
 __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0, int64_t n0,
-                                                     const LmArgs &a, float *red)
+                                                     const LmArgs &a, float *red,
+                                                     const int32_t *tok_s)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -90,10 +93,7 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
             for (int j = 0; j < C::JB; ++j)
                 if (colv[j])
                     m = fmaxf(m, z.v[i][j][r]);
-            m = fmaxf(m, shfl_xor(m, 1));
-            m = fmaxf(m, shfl_xor(m, 2));
-            m = fmaxf(m, shfl_xor(m, 4));
-            m = fmaxf(m, shfl_xor(m, 8));
+            m = row16_max(m);
             if ((lane & 15) == 0)
                 red_m[wc * 128 + tile_row<C>(lane, wr, i, r)] = m;
         }
@@ -120,12 +120,8 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
             float blk[C::JB];
 #pragma unroll
             for (int j = 0; j < C::JB; ++j) {
-                float e = colv[j] ? exp_neg(z.v[i][j][r] - cm[i][r]) : 0.0f;
-                e = e + shfl_xor(e, 1);
-                e = e + shfl_xor(e, 2);
-                e = e + shfl_xor(e, 4);
-                e = e + shfl_xor(e, 8);
-                blk[j] = e;
+                const float e = colv[j] ? exp_neg(z.v[i][j][r] - cm[i][r]) : 0.0f;
+                blk[j] = row16_sum(e);
             }
             const float part = tree_blocks<C>(blk);
             if ((lane & 15) == 0)
@@ -154,10 +150,11 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
     for (int i = 0; i < C::IB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t row = m0 + tile_row<C>(lane, wr, i, r);
+            const int rt = tile_row<C>(lane, wr, i, r);
+            const int64_t row = m0 + rt;
             if (row >= a.M)
                 continue;
-            const int64_t t = a.tok[row];
+            const int64_t t = tok_s[rt];
             const int64_t rel = t - n0 - wc * WCOLS - (lane & 15);
             if (rel >= 0 && rel < WCOLS && (rel & 15) == 0 && t < a.V) {
                 const int j = static_cast<int>(rel >> 4);
@@ -173,18 +170,26 @@ template <class C, int LOG>
 __global__ __launch_bounds__(C::kThreads, 2) void lmhead_fused_kernel(LmArgs a)
 {
     __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
+    __shared__ int32_t tok_s[BM];
     const int tm = static_cast<int>((a.M + BM - 1) / BM);
     const int tn = static_cast<int>(a.nchunk);
     int mt, nt;
     xcd_tile(blockIdx.x, tm * tn, tm, tn, 8, mt, nt);
     const int64_t m0 = static_cast<int64_t>(mt) * BM;
     const int64_t n0 = static_cast<int64_t>(nt) * BN;
+    // The tile's token ids are fetched now and land long before the epilogue
+    // needs them.
+    int32_t tv = -1;
+    if (threadIdx.x < BM && m0 + threadIdx.x < a.M)
+        tv = a.tok[m0 + threadIdx.x];
 
     const Pipe pipe =
         make_pipe<C>(a.H + m0 * a.K, a.M - m0, a.Wvt + n0 * a.K, a.V - n0, a.K, 0);
     Acc<C> z;
     leaf_tree_mainloop<C, LOG>(pipe, a.stages_per_leaf, lds, z);
-    chunk_stats_epilogue<C>(z, m0, n0, a, reinterpret_cast<float *>(lds));
+    if (threadIdx.x < BM)
+        tok_s[threadIdx.x] = tv;
+    chunk_stats_epilogue<C>(z, m0, n0, a, reinterpret_cast<float *>(lds), tok_s);
 }
 
 // Several partitions: fold the partition roots of the logits with the top
@@ -194,8 +199,11 @@ __global__ __launch_bounds__(CfgDual::kThreads) void lmhead_roots_kernel(LmArgs 
 {
     using C = CfgDual;
     __shared__ float red[2 * C::WC * 128];
+    __shared__ int32_t tok_s[BM];
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
     const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+    if (threadIdx.x < BM)
+        tok_s[threadIdx.x] = m0 + threadIdx.x < a.M ? a.tok[m0 + threadIdx.x] : -1;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wr = wave / C::WC, wc = wave % C::WC;
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(CfgDual::kThreads) void lmhead_roots_kernel(LmArgs 
                     rv[q] = a.roots[q * MV + row * a.V + col];
                 z.v[i][j][r] = fold_roots<P>(rv);
             }
-    chunk_stats_epilogue<C>(z, m0, n0, a, red);
+    chunk_stats_epilogue<C>(z, m0, n0, a, red, tok_s);
 }
 
 // Per row: balanced tree over the chunk statistics in chunk order, then
