@@ -14,6 +14,22 @@
 
 namespace iso {
 
+int device_cus()
+{
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 enum OutMode : int { kOutF32 = 0, kOutBF16 = 1, kOutWorkspace = 2 };
 
 constexpr int kTileGroup = 8;  // tile rows per group of the XCD-aware order

@@ -150,6 +150,16 @@ __device__ __forceinline__ void tree_push(Acc<C> (&stk)[LOG > 0 ? LOG : 1], Acc<
     }
 }
 
+// This lane's index in its wave, as a value the compiler must recompute
+// where it is used: persistent kernels loop over tiles, and hoisting every
+// lane-derived address out of that loop costs more registers than it saves.
+__device__ __forceinline__ int lane_id()
+{
+    int l = static_cast<int>(threadIdx.x & 63);
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
 {
@@ -200,7 +210,7 @@ __device__ __forceinline__ Pipe make_pipe(const uint16_t *A_tile, int64_t rowsA,
 {
     static_assert(C::kDma <= kMaxDma, "too many loads per wave");
     Pipe p;
-    const int lane = threadIdx.x & 63;
+    const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     p.ra = tile_rsrc(A_tile, rowsA < BM ? rowsA : BM, K);
     p.rb = tile_rsrc(B_tile, rowsB < BN ? rowsB : BN, K);
@@ -276,19 +286,35 @@ __device__ __forceinline__ void frag_wait(Frags<C> &f)
         asm volatile("" : "+v"(f.b[j]));
 }
 
+// First NBUF-1 stages of a tile's ring (`nst` stages in all).  A persistent
+// kernel issues them for its next tile as soon as the current tile's main
+// loop has returned, so that their latency overlaps the epilogue.
+template <class C>
+__device__ __forceinline__ void pipe_prologue(const Pipe &p, char *lds, int nst)
+{
+#pragma unroll
+    for (int s = 0; s < C::NBUF - 1; ++s)
+        if (s < nst)
+            stage_dma<C>(p, lds, s, s);
+}
+
 // The contraction of one tile over 2^LOG leaves of `spl` stages (64 columns
-// of K) each.  On return `root` holds the subtree root in the MFMA output
-// layout, every buffer load has landed and all waves have passed a final
-// barrier, so `lds` may be reused by the caller.
-template <class C, int LOG>
+// of K) each.  With PROLOGUE false the caller has already issued
+// pipe_prologue for this tile (and nothing else on the ring since).  On
+// return `root` holds the subtree root in the MFMA output layout, every
+// buffer load has landed and all waves have passed a final barrier, so `lds`
+// may be reused by the caller.  Global stores or loads that the caller has in
+// flight only make the ring's vmcnt waits stricter (loads complete in order,
+// so "at most n outstanding" still implies that the oldest stage landed).
+template <class C, int LOG, bool PROLOGUE = true>
 __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char *lds,
                                                    Acc<C> &root)
 {
     constexpr int LP = 1 << LOG;
     constexpr int NB = C::NBUF;
     const int nst = LP * spl;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / C::WC;
     const int wc = wave % C::WC;
 
@@ -299,10 +325,8 @@ __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char 
     const uint32_t rowb =
         (uint32_t)kBOffset + (uint32_t)(wc * (BN / C::WC) + (lane & 15)) * kRowBytes;
 
-#pragma unroll
-    for (int s = 0; s < NB - 1; ++s)
-        if (s < nst)
-            stage_dma<C>(p, lds, s, s);
+    if constexpr (PROLOGUE)
+        pipe_prologue<C>(p, lds, nst);
 
     Acc<C> stk[LOG > 0 ? LOG : 1];
     Acc<C> acc;
@@ -371,8 +395,8 @@ template <class C>
 __device__ __forceinline__ const float *stage_tile(const Acc<C> &root, char *lds)
 {
     static_assert(C::kLdsBytes >= BM * BN * 4, "the stage ring must hold the FP32 tile");
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / C::WC, wc = wave % C::WC;
     float *stage = reinterpret_cast<float *>(lds);
 #pragma unroll
@@ -475,13 +499,10 @@ __device__ __forceinline__ void store_tile(const Acc<C> &root, char *lds, void *
 // i.e. a compact block of output tiles whose A rows and B columns its L2
 // shares.  Returns the tile's (row block, column block) in a tm x tn grid.
 constexpr int kXcds = 8;
-__device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tm, int tn, int group,
-                                         int &mt, int &nt)
+
+// Tile t of the grouped order: G tile rows at a time, rows fastest.
+__device__ __forceinline__ void grouped_tile(int t, int tm, int tn, int group, int &mt, int &nt)
 {
-    const int xcd = bid % kXcds;
-    const int per = nblocks / kXcds;
-    const int extra = nblocks % kXcds;
-    const int t = xcd * per + (xcd < extra ? xcd : extra) + bid / kXcds;
     const int gsz_full = group * tn;
     const int g = t / gsz_full;
     const int first = g * group;
@@ -489,6 +510,24 @@ __device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tm, int tn, i
     const int r = t % gsz_full;
     mt = first + r % rows;
     nt = r / rows;
+}
+
+__device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tm, int tn, int group,
+                                         int &mt, int &nt)
+{
+    const int xcd = bid % kXcds;
+    const int per = nblocks / kXcds;
+    const int extra = nblocks % kXcds;
+    const int t = xcd * per + (xcd < extra ? xcd : extra) + bid / kXcds;
+    grouped_tile(t, tm, tn, group, mt, nt);
+}
+
+// Workgroup barrier for code that has global loads in flight which the
+// barrier must not wait for (__syncthreads() may also drain the vector
+// memory counter): LDS operations complete first, then all waves meet.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Fixed tree over P partition roots (P = 1, 2, 4, 8), lower index left.

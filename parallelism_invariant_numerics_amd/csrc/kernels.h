@@ -12,6 +12,10 @@ namespace iso {
 // Leaf/tree GEMM over `parts` contiguous leaf blocks of `leaves_per_part`
 // leaves (1..16) each.  mode 0: FP32 C [M][N]; 1: bf16 C; 2: FP32 partition
 // roots ws[parts][M][N].
+// Compute units of the current device (cached per device; 256 when the
+// query fails).  Persistent kernels size their grids with it.
+int device_cus();
+
 hipError_t launch_gemm_partials(const uint16_t *A, const uint16_t *Wt, void *out, int mode,
                                 int64_t M, int64_t N, int64_t K, int leaves_per_part,
                                 int leaf_size, int parts, hipStream_t stream);

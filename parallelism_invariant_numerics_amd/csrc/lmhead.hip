@@ -71,8 +71,8 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
                                                      const LmArgs &a, float *red,
                                                      const int32_t *tok_s)
 {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / C::WC, wc = wave % C::WC;
     const int64_t chunk = n0 / kChunk;
     float *red_m = red;
@@ -97,37 +97,30 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
             if ((lane & 15) == 0)
                 red_m[wc * 128 + tile_row<C>(lane, wr, i, r)] = m;
         }
-    __syncthreads();
+    lds_barrier();
 
-    float cm[C::IB][4];
+    // exp-sums: 16-column blocks by lane butterfly, then blocks, then waves;
+    // the chunk maximum of each row is read back where it is needed
 #pragma unroll
     for (int i = 0; i < C::IB; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int rt = tile_row<C>(lane, wr, i, r);
-            float m = red_m[rt];
+            float cm = red_m[rt];
 #pragma unroll
             for (int q = 1; q < C::WC; ++q)
-                m = fmaxf(m, red_m[q * 128 + rt]);
-            cm[i][r] = m;
-        }
-
-    // exp-sums: 16-column blocks by lane butterfly, then blocks, then waves
-#pragma unroll
-    for (int i = 0; i < C::IB; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+                cm = fmaxf(cm, red_m[q * 128 + rt]);
             float blk[C::JB];
 #pragma unroll
             for (int j = 0; j < C::JB; ++j) {
-                const float e = colv[j] ? exp_neg(z.v[i][j][r] - cm[i][r]) : 0.0f;
+                const float e = colv[j] ? exp_neg(z.v[i][j][r] - cm) : 0.0f;
                 blk[j] = row16_sum(e);
             }
             const float part = tree_blocks<C>(blk);
             if ((lane & 15) == 0)
                 red_s[wc * 128 + tile_row<C>(lane, wr, i, r)] = part;
         }
-    __syncthreads();
+    lds_barrier();
 
     if (wc == 0 && (lane & 15) == 0) {
 #pragma unroll
@@ -137,8 +130,12 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
                 const int rt = tile_row<C>(lane, wr, i, r);
                 const int64_t row = m0 + rt;
                 if (row < a.M) {
+                    float cm = red_m[rt];
+#pragma unroll
+                    for (int q = 1; q < C::WC; ++q)
+                        cm = fmaxf(cm, red_m[q * 128 + rt]);
                     float *st = a.stats + (row * a.nchunk + chunk) * 2;
-                    st[0] = cm[i][r];
+                    st[0] = cm;
                     st[1] = tree_waves<C>(red_s, rt);
                 }
             }
@@ -166,30 +163,84 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
         }
 }
 
+// Origin and operand pipe of tile t of the grouped order.
+template <class C>
+__device__ __forceinline__ Pipe lm_tile(const LmArgs &a, int t, int tm, int tn, int64_t &m0,
+                                        int64_t &n0)
+{
+    int mt, nt;
+    grouped_tile(t, tm, tn, 8, mt, nt);
+    m0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(mt)) * BM;
+    n0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(nt)) * BN;
+    return make_pipe<C>(a.H + m0 * a.K, a.M - m0, a.Wvt + n0 * a.K, a.V - n0, a.K, 0);
+}
+
+// The sampled token ids of tile rows m0 .. m0+127 into dst (LDS), by direct
+// global-to-LDS loads of the first two waves; rows at or past M read as 0
+// (they are never used).  Tracked by the vector memory counter like the
+// operand stages.
+__device__ __forceinline__ void tok_dma(const LmArgs &a, int64_t m0, int32_t *dst)
+{
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w < BM / 64) {
+        const int64_t rows = a.M - m0 < BM ? a.M - m0 : BM;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(a.tok + m0), (short)0, static_cast<int>(rows * 4), 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ISO_LDS void *)(dst + 64 * w), 4,
+                                                 static_cast<uint32_t>(lane_id() * 4),
+                                                 static_cast<uint32_t>(w * 256), 0, 0);
+    }
+}
+
+// Persistent: the workgroups on XCD x take the contiguous range
+// [x per, (x+1) per) of the grouped tile order (so the tiles running together
+// on one L2 share hidden rows and vocabulary rows), stepping by the number of
+// workgroups per XCD.  The next tile's first stages and token ids are
+// requested before the current tile's softmax epilogue, which hides their
+// latency.  Nothing but loads to LDS is in flight across the epilogue, and
+// nothing is carried in vector registers from one tile to the next.
 template <class C, int LOG>
 __global__ __launch_bounds__(C::kThreads, 2) void lmhead_fused_kernel(LmArgs a)
 {
     __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
-    __shared__ int32_t tok_s[BM];
+    __shared__ float red[2 * C::WC * 128];
+    __shared__ int32_t tok_s[2][BM];
     const int tm = static_cast<int>((a.M + BM - 1) / BM);
     const int tn = static_cast<int>(a.nchunk);
-    int mt, nt;
-    xcd_tile(blockIdx.x, tm * tn, tm, tn, 8, mt, nt);
-    const int64_t m0 = static_cast<int64_t>(mt) * BM;
-    const int64_t n0 = static_cast<int64_t>(nt) * BN;
-    // The tile's token ids are fetched now and land long before the epilogue
-    // needs them.
-    int32_t tv = -1;
-    if (threadIdx.x < BM && m0 + threadIdx.x < a.M)
-        tv = a.tok[m0 + threadIdx.x];
+    const int total = tm * tn;
+    const int xcd = blockIdx.x % kXcds;
+    const int slots = gridDim.x / kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
+    int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds;
+    if (w >= end)
+        return;
+    const int nst = (1 << LOG) * a.stages_per_leaf;
 
-    const Pipe pipe =
-        make_pipe<C>(a.H + m0 * a.K, a.M - m0, a.Wvt + n0 * a.K, a.V - n0, a.K, 0);
-    Acc<C> z;
-    leaf_tree_mainloop<C, LOG>(pipe, a.stages_per_leaf, lds, z);
-    if (threadIdx.x < BM)
-        tok_s[threadIdx.x] = tv;
-    chunk_stats_epilogue<C>(z, m0, n0, a, reinterpret_cast<float *>(lds), tok_s);
+    int64_t m0, n0;
+    {
+        const Pipe p0 = lm_tile<C>(a, w, tm, tn, m0, n0);
+        tok_dma(a, m0, tok_s[0]);
+        pipe_prologue<C>(p0, lds, nst);
+    }
+    for (int it = 0;; ++it) {
+        Acc<C> z;
+        {
+            const Pipe pipe = lm_tile<C>(a, w, tm, tn, m0, n0);
+            leaf_tree_mainloop<C, LOG, false>(pipe, a.stages_per_leaf, lds, z);
+        }
+        const int wn = w + slots;
+        if (wn < end) {
+            int64_t m0n, n0n;
+            const Pipe pn = lm_tile<C>(a, wn, tm, tn, m0n, n0n);
+            tok_dma(a, m0n, tok_s[(it + 1) & 1]);
+            pipe_prologue<C>(pn, lds, nst);
+        }
+        chunk_stats_epilogue<C>(z, m0, n0, a, red, tok_s[it & 1]);
+        if (wn >= end)
+            break;
+        w = wn;
+    }
 }
 
 // Several partitions: fold the partition roots of the logits with the top
@@ -205,7 +256,7 @@ __global__ __launch_bounds__(CfgDual::kThreads) void lmhead_roots_kernel(LmArgs 
     if (threadIdx.x < BM)
         tok_s[threadIdx.x] = m0 + threadIdx.x < a.M ? a.tok[m0 + threadIdx.x] : -1;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / C::WC, wc = wave % C::WC;
     const int64_t MV = a.M * a.V;
     Acc<C> z;
@@ -272,7 +323,7 @@ __global__ __launch_bounds__(256) void lmhead_finish_kernel(const float *stats,
         wm[tid >> 6] = mv;
         ws[tid >> 6] = sv;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         float m01 = wm[0], s01 = ws[0];
         lse_merge(m01, s01, wm[1], ws[1]);
@@ -293,7 +344,11 @@ template <int LOG>
 static hipError_t launch_fused(const LmArgs &a, hipStream_t stream)
 {
     using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
-    dim3 grid(static_cast<unsigned>(((a.M + BM - 1) / BM) * a.nchunk));
+    const int64_t tiles = ((a.M + BM - 1) / BM) * a.nchunk;
+    const int64_t slots = static_cast<int64_t>(device_cus()) * (C::kWaves == 4 ? 2 : 1);
+    int64_t g = tiles < slots ? tiles : slots;
+    g = (g + kXcds - 1) / kXcds * kXcds;  // whole rounds over the XCDs
+    dim3 grid(static_cast<unsigned>(g));
     hipLaunchKernelGGL((lmhead_fused_kernel<C, LOG>), grid, dim3(C::kThreads), 0, stream, a);
     return hipGetLastError();
 }

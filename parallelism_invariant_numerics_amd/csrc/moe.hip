@@ -267,7 +267,7 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(MoeGemmArgs 
 {
     __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / C::WC, wc = wave % C::WC;
     constexpr int TN = GATE_UP ? kGuCols : BN;  // output columns per tile
     const int ntn = static_cast<int>((a.N + TN - 1) / TN);
@@ -372,7 +372,8 @@ template <int LOG, bool GU>
 static void launch_expert(const MoeGemmArgs &a, hipStream_t stream)
 {
     using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
-    const unsigned grid = LOG <= 1 ? 512 : 256;  // resident workgroups on 256 CUs
+    // resident workgroups, a multiple of 8
+    const unsigned grid = static_cast<unsigned>(device_cus() / kXcds * kXcds * (LOG <= 1 ? 2 : 1));
     static_assert(kXcds == 8, "the task split assumes a grid that is a multiple of 8");
     hipLaunchKernelGGL((moe_expert_kernel<C, LOG, GU>), dim3(grid), dim3(C::kThreads), 0, stream,
                        a);
