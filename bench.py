@@ -42,6 +42,9 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true",
                    help="headline GEMM launches only (for rocprofv3 runs)")
+    p.add_argument("--settle", type=float, default=0.3,
+                   help="seconds of untimed back-to-back launches before each timing "
+                        "(clocks ramp up under sustained load); 0 for counter runs")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one plain copy kernel over 256 MiB (HBM counter calibration)")
     return p.parse_args()
@@ -52,12 +55,17 @@ def _dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
-def _settle(fn, seconds=0.3):
+SETTLE_S = 0.3
+
+
+def _settle(fn, seconds=None):
     """Run fn back to back for about `seconds` of wall time, untimed.  The
     GPU raises its clocks only after some tens of milliseconds of sustained
     load; a few warmup steps of a 50 us kernel would time the ramp instead of
     the steady state."""
     import torch
+    if seconds is None:
+        seconds = SETTLE_S
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(50):
@@ -70,7 +78,8 @@ def _time_events(fn, steps, stream):
     `steps` back-to-back calls (the launches queue up, so host-side call
     overhead does not appear as idle GPU time between them)."""
     import torch
-    _settle(fn, 0.2)
+    _settle(fn, 0.66 * SETTLE_S)
+    fn()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -130,6 +139,8 @@ def _cpu_baseline(cfg, target_s=12.0):
 
 def main():
     args = _args()
+    global SETTLE_S
+    SETTLE_S = max(0.0, args.settle)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
