@@ -522,6 +522,37 @@ __device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tm, int tn, i
     grouped_tile(t, tm, tn, group, mt, nt);
 }
 
+// LDS access in inline assembly, for code that runs while direct
+// global-to-LDS loads are in flight: the compiler would otherwise make every
+// LDS access there wait for them (it cannot tell the buffers apart).  Reads
+// are issued, then lds_wait() completes them and pins the results, so that
+// no use is scheduled before the wait.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(ISO_LDS const char *)p;
+}
+__device__ __forceinline__ void lds_write_f32(uint32_t addr, float v)
+{
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_issue_b128(f32x4 &v, uint32_t addr)
+{
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+}
+__device__ __forceinline__ void lds_issue_b32(int32_t &v, uint32_t addr)
+{
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+}
+__device__ __forceinline__ void lds_wait()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+template <class T>
+__device__ __forceinline__ void lds_pin(T &v)
+{
+    asm volatile("" : "+v"(v));
+}
+
 // Workgroup barrier for code that has global loads in flight which the
 // barrier must not wait for (__syncthreads() may also drain the vector
 // memory counter): LDS operations complete first, then all waves meet.

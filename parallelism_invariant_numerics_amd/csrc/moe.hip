@@ -143,44 +143,83 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *logits, int
 // --------------------------------------------------------------- bucket
 
 // Expert e = blockIdx.x gathers the entries i = t * top_k + slot with
-// idx[i] == e, in increasing i, into rows[e][0 .. count).  Each pass covers
-// 2048 entries: thread j owns entries [8j, 8j + 8) of the pass; an exclusive
-// scan of the per-thread match counts gives every match its ordered slot.
+// idx[i] == e, in increasing i, into rows[e][0 .. count).  The entries go
+// through LDS in chunks of 32768 (direct global-to-LDS loads, all in flight
+// together).  In a chunk, wave w scans the contiguous quarter w, 64 entries
+// at a time; a ballot ranks each match among the wave's matches (lanes below
+// it).  A first pass counts the matches of every quarter, so that quarter w
+// starts after the matches of quarters 0 .. w-1; the second pass writes.
+constexpr int kBucketChunk = 32768;
+
 __global__ __launch_bounds__(256) void moe_bucket_kernel(const int32_t *idx, int32_t *rows,
                                                          int32_t *counts, int64_t n_entries,
                                                          int64_t T)
 {
-    __shared__ int scan[256];
+    __shared__ __attribute__((aligned(16))) int32_t sidx[kBucketChunk];
+    __shared__ int wcount[4];
     const int e = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t below = (1ull << lane) - 1;
     int32_t *dst = rows + static_cast<int64_t>(e) * T;
     int count = 0;
-    for (int64_t base = 0; base < n_entries; base += 2048) {
-        const int64_t i0 = base + static_cast<int64_t>(tid) * 8;
-        unsigned mask = 0;
+    for (int64_t base = 0; base < n_entries; base += kBucketChunk) {
+        const int n = n_entries - base < kBucketChunk ? static_cast<int>(n_entries - base)
+                                                       : kBucketChunk;
+        // 128 KiB: each wave loads 32 KiB, 1 KiB per instruction; entries
+        // past n read as 0 and are never scanned
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(idx + base), (short)0, n * 4, 0x00020000);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (i0 + j < n_entries && idx[i0 + j] == e)
-                mask |= 1u << j;
-        const int mine = __popc(mask);
-        scan[tid] = mine;
-        __syncthreads();
-        // inclusive Hillis-Steele scan over the 256 counts
-        for (int d = 1; d < 256; d <<= 1) {
-            const int add = tid >= d ? scan[tid - d] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
+        for (int j = 0; j < kBucketChunk / 1024; ++j) {
+            const int off = w * kBucketChunk + j * 1024;  // bytes: wave w's 32 KiB, then 1 KiB steps
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (ISO_LDS void *)(reinterpret_cast<char *>(sidx) + off), 16,
+                static_cast<uint32_t>(lane * 16), static_cast<uint32_t>(off), 0, 0);
         }
-        int pos = count + scan[tid] - mine;
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        const int q = ((n + 255) / 256) * 64;  // entries per quarter, a multiple of 64
+        const int lo = w * q;
+        const int hi = lo + q < n ? lo + q : n;
+        constexpr int U = 8;  // independent LDS reads per step
+        int c = 0;
+        for (int i0 = lo; i0 < hi; i0 += 64 * U) {
+            bool m[U];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (mask & (1u << j))
-                dst[pos++] = static_cast<int32_t>(i0 + j);
-        count += scan[255];
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + 64 * u + lane;
+                m[u] = i < hi && sidx[i < kBucketChunk ? i : 0] == e;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                c += __popcll(__ballot(m[u]));
+        }
+        if (lane == 0)
+            wcount[w] = c;
         __syncthreads();
+        int pos = count;
+        for (int k = 0; k < w; ++k)
+            pos += wcount[k];
+        for (int i0 = lo; i0 < hi; i0 += 64 * U) {
+            bool m[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + 64 * u + lane;
+                m[u] = i < hi && sidx[i < kBucketChunk ? i : 0] == e;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t mask = __ballot(m[u]);
+                if (m[u])
+                    dst[pos + __popcll(mask & below)] =
+                        static_cast<int32_t>(base + i0 + 64 * u + lane);
+                pos += __popcll(mask);
+            }
+        }
+        count += (wcount[0] + wcount[1]) + (wcount[2] + wcount[3]);
+        __syncthreads();  // the next chunk overwrites sidx and wcount
     }
-    if (tid == 0)
+    if (threadIdx.x == 0)
         counts[e] = count;
 }
 
@@ -229,31 +268,41 @@ struct MoeGemmArgs {
     int stages_per_leaf;
 };
 
-// Pipe over gathered A rows: DMA row r of the tile reads source row
-// rows_e[m0 + r] / row_div of the whole A matrix, or zero when r >= nvalid
-// (its offset lies past the buffer's range).
-template <class C>
-__device__ __forceinline__ Pipe make_pipe_gather(const MoeGemmArgs &a, const int32_t *rows_e,
-                                                 int m0, int nvalid, const uint16_t *B_tile,
-                                                 int64_t rowsB)
+// One work item: an expert's 128-row tile (rows m0 .. m0+nvalid-1 of its
+// bucket) times output columns n0 .. n0+TN-1.
+struct MoeTask {
+    int e, m0, nvalid;
+    int64_t n0;
+};
+
+__device__ __forceinline__ MoeTask moe_task(const int32_t *__restrict__ tiles,
+                                            const int32_t *__restrict__ counts, int w, int ntn,
+                                            int tn_cols)
 {
-    Pipe p = make_pipe<C>(a.A, 0, B_tile, rowsB, a.K, 0);
-    p.ra = tile_rsrc(a.A, a.a_rows_total, a.K);
-    const int lane = threadIdx.x & 63;
+    MoeTask t;
+    const int tile = w / ntn;
+    t.n0 = static_cast<int64_t>(w % ntn) * tn_cols;
+    t.e = __builtin_amdgcn_readfirstlane(tiles[2 * tile]);
+    t.m0 = __builtin_amdgcn_readfirstlane(tiles[2 * tile + 1]);
+    const int cnt = __builtin_amdgcn_readfirstlane(counts[t.e]);
+    t.nvalid = cnt - t.m0 < BM ? cnt - t.m0 : BM;
+    return t;
+}
+
+// The task's bucket entries rows[e][m0 .. m0+127] into dst (LDS) by direct
+// global-to-LDS loads of the first two waves; entries past the bucket read
+// as 0 and are never used.  Tracked by the vector memory counter.
+__device__ __forceinline__ void rows_dma(const MoeGemmArgs &a, const MoeTask &t, int32_t *dst)
+{
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t c = (lane & 7) ^ (lane >> 3);
-    const uint32_t oob = (uint32_t)(a.a_rows_total * a.K * 2);
-#pragma unroll
-    for (int i = 0; i < C::kDma; ++i) {
-        const int r = C::kDma * 8 * w + 8 * i + (lane >> 3);
-        if (r < nvalid) {
-            const int64_t src = rows_e[m0 + r] / a.row_div;
-            p.voffa[i] = (uint32_t)(src * a.K * 2) + c * 16;
-        } else {
-            p.voffa[i] = oob;
-        }
+    if (w < BM / 64) {
+        const int32_t *src = a.rows + static_cast<int64_t>(t.e) * a.T + t.m0;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(src), (short)0, t.nvalid * 4, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ISO_LDS void *)(dst + 64 * w), 4,
+                                                 static_cast<uint32_t>(lane_id() * 4),
+                                                 static_cast<uint32_t>(w * 256), 0, 0);
     }
-    return p;
 }
 
 // Gate/up tiles hold 64 intermediate columns: B rows 0..63 of the tile are
@@ -262,67 +311,126 @@ __device__ __forceinline__ Pipe make_pipe_gather(const MoeGemmArgs &a, const int
 // tile columns 0..63 and U in columns 64..127 of every row.
 constexpr int kGuCols = BN / 2;
 
-template <class C, int LOG, bool GATE_UP>
-__global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(MoeGemmArgs a)
+// Pipe over gathered A rows: DMA row r of the tile reads source row
+// rows_s[r] / row_div of the whole A matrix, or zero when r >= nvalid (its
+// offset lies past the buffer's range).  rows_s: the task's entries in LDS.
+template <class C, bool GATE_UP>
+__device__ __forceinline__ Pipe moe_pipe(const MoeGemmArgs &a, const MoeTask &t,
+                                         const int32_t *rows_s)
 {
-    __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
-    const int lane = threadIdx.x & 63;
+    const int64_t boff = static_cast<int64_t>(t.e) * a.N * a.K + t.n0 * a.K;
+    Pipe p = make_pipe<C>(a.A, 0, a.B0 + boff, a.N - t.n0, a.K, 0);
+    p.ra = tile_rsrc(a.A, a.a_rows_total, a.K);
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t c = (lane & 7) ^ (lane >> 3);
+    const uint32_t oob = (uint32_t)(a.a_rows_total * a.K * 2);
+    int32_t ent[C::kDma];
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i)
+        lds_issue_b32(ent[i], lds_addr(rows_s + C::kDma * 8 * w + 8 * i + (lane >> 3)));
+    lds_wait();
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i) {
+        lds_pin(ent[i]);
+        const int r = C::kDma * 8 * w + 8 * i + (lane >> 3);
+        if (r < t.nvalid) {
+            const int64_t src = ent[i] / a.row_div;
+            p.voffa[i] = (uint32_t)(src * a.K * 2) + c * 16;
+        } else {
+            p.voffa[i] = oob;
+        }
+    }
+    if constexpr (GATE_UP) {
+        const int64_t brows = a.N - t.n0 < kGuCols ? a.N - t.n0 : kGuCols;
+        p.rb = tile_rsrc((w < C::kWaves / 2 ? a.B0 : a.B1) + boff, brows, a.K);
+#pragma unroll
+        for (int i = 0; i < C::kDma; ++i) {
+            const uint32_t r = (C::kDma * 8 * w + 8 * i + (lane >> 3)) & (kGuCols - 1);
+            p.voffb[i] = (uint32_t)((int64_t)r * a.K * 2) + c * 16;
+        }
+    }
+    return p;
+}
+
+// Rows 64h .. 64h+63 of a tile's roots (held by the waves of tile row h) into
+// `stg` [64][128] FP32, with the chunk swizzle of stage_tile.
+template <class C>
+__device__ __forceinline__ void stage_half(const Acc<C> &root, float *stg, int h)
+{
+    static_assert(C::WR == 2 && BM == 128, "two wave rows of 64 tile rows");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / C::WC, wc = wave % C::WC;
-    constexpr int TN = GATE_UP ? kGuCols : BN;  // output columns per tile
-    const int ntn = static_cast<int>((a.N + TN - 1) / TN);
-    const int total = __builtin_amdgcn_readfirstlane(*a.ntiles) * ntn;
-    // XCD-aware work split: the workgroups on XCD x (blockIdx % 8 == x) take
-    // the contiguous task range [x per, (x+1) per), so the tasks running
-    // together on one L2 share an expert's weights and a tile's rows.  The
-    // grid is a multiple of 8, so every task is taken exactly once.
-    const int xcd = blockIdx.x % kXcds;
-    const int slots = gridDim.x / kXcds;
-    const int per = (total + kXcds - 1) / kXcds;
-    const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
-    for (int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds; w < end; w += slots) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous tile's stores drained
-        const int tile = w / ntn;
-        const int64_t n0 = static_cast<int64_t>(w % ntn) * TN;
-        const int e = __builtin_amdgcn_readfirstlane(a.tiles[2 * tile]);
-        const int m0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * tile + 1]);
-        const int cnt = __builtin_amdgcn_readfirstlane(a.counts[e]);
-        const int nvalid = cnt - m0 < BM ? cnt - m0 : BM;
-        const int32_t *rows_e = a.rows + static_cast<int64_t>(e) * a.T;
-        const int64_t boff = static_cast<int64_t>(e) * a.N * a.K + n0 * a.K;
-
-        Pipe p = make_pipe_gather<C>(a, rows_e, m0, nvalid, a.B0 + boff, a.N - n0);
-        if constexpr (GATE_UP) {
-            const int wu = __builtin_amdgcn_readfirstlane(wave);
-            const int64_t brows = a.N - n0 < kGuCols ? a.N - n0 : kGuCols;
-            p.rb = tile_rsrc((wu < C::kWaves / 2 ? a.B0 : a.B1) + boff, brows, a.K);
-            const uint32_t c = (lane & 7) ^ (lane >> 3);
+    if (wr != h)
+        return;
+    const int lane = lane_id();
 #pragma unroll
-            for (int i = 0; i < C::kDma; ++i) {
-                const uint32_t r = (C::kDma * 8 * wu + 8 * i + (lane >> 3)) & (kGuCols - 1);
-                p.voffb[i] = (uint32_t)((int64_t)r * a.K * 2) + c * 16;
+    for (int i = 0; i < C::IB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::JB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = tile_row<C>(lane, wr, i, r) - 64 * h;
+                const int col = tile_col<C>(lane, wc, j);
+                const int chunk = (col >> 2) ^ (((row >> 2) & 3) << 2);
+                lds_write_f32(lds_addr(stg + row * 128 + chunk * 4 + (col & 3)), root.v[i][j][r]);
             }
-        }
-        Acc<C> r0;
-        leaf_tree_mainloop<C, LOG>(p, a.stages_per_leaf, lds, r0);
+}
 
+// Columns 4c .. 4c+3 of row `row` of a [64][128] staging buffer (address).
+__device__ __forceinline__ uint32_t staged_addr(const float *stg, int row, int c)
+{
+    return lds_addr(stg + row * 128 + ((c ^ (((row >> 2) & 3) << 2)) << 2));
+}
+
+// Epilogue of one task: gate/up writes h = bf16(silu(G) U) (G in tile
+// columns 0..63, U in 64..127), down writes the FP32 roots; tile row r goes
+// to output row rows_s[r].  Two halves of 64 rows through `stg` (32 KiB).
+template <class C, bool GATE_UP>
+__device__ __forceinline__ void moe_epilogue(const MoeGemmArgs &a, const MoeTask &t,
+                                             const Acc<C> &r0, const int32_t *rows_s, float *stg)
+{
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        stage_half<C>(r0, stg, h);
+        lds_barrier();
         if constexpr (GATE_UP) {
-            // h = bf16(silu(G) * U), G in tile columns 0..63, U in 64..127.
-            const float *stage = stage_tile<C>(r0, lds);
+            constexpr int UPT = 64 * (kGuCols / 8) / C::kThreads;  // units per thread
             const float kLog2e = 1.44269504088896340736f;
-            uint16_t *o = static_cast<uint16_t *>(a.out) + n0;
+            uint16_t *o = static_cast<uint16_t *>(a.out) + t.n0;
             const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (a.N % 8 == 0);
-            const int cmax = a.N - n0 < kGuCols ? static_cast<int>(a.N - n0) : kGuCols;
-            for (int u = threadIdx.x; u < BM * (kGuCols / 8); u += C::kThreads) {
+            const int cmax = a.N - t.n0 < kGuCols ? static_cast<int>(a.N - t.n0) : kGuCols;
+            constexpr int NB = UPT < 2 ? UPT : 2;  // units per LDS round trip
+#pragma unroll
+            for (int kb = 0; kb < UPT; kb += NB) {
+            f32x4 g0[NB], g1[NB], u0[NB], u1[NB];
+            int32_t dst[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int u = threadIdx.x + (kb + k) * C::kThreads;
                 const int row = u >> 3, q = u & 7;
-                if (row >= nvalid)
-                    break;
-                const f32x4 g0 = staged_chunk(stage, row, 2 * q);
-                const f32x4 g1 = staged_chunk(stage, row, 2 * q + 1);
-                const f32x4 u0 = staged_chunk(stage, row, kGuCols / 4 + 2 * q);
-                const f32x4 u1 = staged_chunk(stage, row, kGuCols / 4 + 2 * q + 1);
-                const float gs[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-                const float us[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                lds_issue_b128(g0[k], staged_addr(stg, row, 2 * q));
+                lds_issue_b128(g1[k], staged_addr(stg, row, 2 * q + 1));
+                lds_issue_b128(u0[k], staged_addr(stg, row, kGuCols / 4 + 2 * q));
+                lds_issue_b128(u1[k], staged_addr(stg, row, kGuCols / 4 + 2 * q + 1));
+                lds_issue_b32(dst[k], lds_addr(rows_s + 64 * h + row));
+            }
+            lds_wait();
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                lds_pin(g0[k]);
+                lds_pin(g1[k]);
+                lds_pin(u0[k]);
+                lds_pin(u1[k]);
+                lds_pin(dst[k]);
+                const int u = threadIdx.x + (kb + k) * C::kThreads;
+                const int row = u >> 3, q = u & 7;
+                if (64 * h + row >= t.nvalid)
+                    continue;
+                const float gs[8] = {g0[k][0], g0[k][1], g0[k][2], g0[k][3],
+                                     g1[k][0], g1[k][1], g1[k][2], g1[k][3]};
+                const float us[8] = {u0[k][0], u0[k][1], u0[k][2], u0[k][3],
+                                     u1[k][0], u1[k][1], u1[k][2], u1[k][3]};
                 float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -330,14 +438,111 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(MoeGemmArgs 
                     const float sg = gs[e] / (1.0f + ex);
                     v[e] = sg * us[e];
                 }
-                const int64_t dst = rows_e[m0 + row];
-                store8_bf16(o + dst * a.N + 8 * q, v, al && 8 * q + 8 <= cmax, cmax - 8 * q);
+                store8_bf16(o + static_cast<int64_t>(dst[k]) * a.N + 8 * q, v,
+                            al && 8 * q + 8 <= cmax, cmax - 8 * q);
+            }
             }
         } else {
-            store_tile<C>(r0, lds, static_cast<float *>(a.out) + n0, a.N, nvalid, a.N - n0, false,
-                          rows_e + m0);
+            constexpr int UPT = 64 * 32 / C::kThreads;  // units per thread
+            float *o = static_cast<float *>(a.out) + t.n0;
+            const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (a.N % 4 == 0);
+            const int cmax = a.N - t.n0 < BN ? static_cast<int>(a.N - t.n0) : BN;
+            constexpr int NB = UPT < 4 ? UPT : 4;  // units per LDS round trip
+#pragma unroll
+            for (int kb = 0; kb < UPT; kb += NB) {
+            f32x4 v[NB];
+            int32_t dst[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const int u = threadIdx.x + (kb + k) * C::kThreads;
+                const int row = u >> 5, q = u & 31;
+                lds_issue_b128(v[k], staged_addr(stg, row, q));
+                lds_issue_b32(dst[k], lds_addr(rows_s + 64 * h + row));
+            }
+            lds_wait();
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                lds_pin(v[k]);
+                lds_pin(dst[k]);
+                const int u = threadIdx.x + (kb + k) * C::kThreads;
+                const int row = u >> 5, q = u & 31;
+                if (64 * h + row >= t.nvalid)
+                    continue;
+                store4_f32(o + static_cast<int64_t>(dst[k]) * a.N + 4 * q, v[k],
+                           al && 4 * q + 4 <= cmax, cmax - 4 * q);
+            }
+            }
         }
-        __syncthreads();  // the next tile's loads overwrite the LDS
+        lds_barrier();
+    }
+}
+
+// Persistent over the task list.  XCD-aware split: the workgroups on XCD x
+// (blockIdx % 8 == x) take the contiguous task range [x per, (x+1) per), so
+// the tasks running together on one L2 share an expert's weights and a
+// tile's rows; the grid is a multiple of 8, so every task is taken once.
+//
+// OVERLAP (eight-wave shape, three-stage ring): the next task's bucket
+// entries are fetched during the current main loop, and its first ring
+// stages are requested right after it, before the epilogue, which stages
+// through its own LDS.  Otherwise (four-wave shape, two workgroups per CU)
+// each task runs start to end and the epilogue stages through the ring.
+template <class C, int LOG, bool GATE_UP>
+__global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(
+    MoeGemmArgs a, const int32_t *__restrict__ tiles, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ ntiles)
+{
+    constexpr bool OVERLAP = C::kWaves == 8;
+    __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
+    __shared__ __attribute__((aligned(16))) float stg_own[OVERLAP ? 64 * 128 : 4];
+    __shared__ int32_t rows_s[2][BM];
+    static_assert(OVERLAP || C::kLdsBytes >= 64 * 128 * 4, "the ring must hold half a tile");
+    float *stg = OVERLAP ? stg_own : reinterpret_cast<float *>(lds);
+
+    constexpr int TN = GATE_UP ? kGuCols : BN;  // output columns per tile
+    const int ntn = static_cast<int>((a.N + TN - 1) / TN);
+    const int total = __builtin_amdgcn_readfirstlane(*ntiles) * ntn;
+    const int xcd = blockIdx.x % kXcds;
+    const int slots = gridDim.x / kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
+    int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds;
+    if (w >= end)
+        return;
+    const int nst = (1 << LOG) * a.stages_per_leaf;
+
+    {
+        const MoeTask t = moe_task(tiles, counts, w, ntn, TN);
+        rows_dma(a, t, rows_s[0]);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if constexpr (OVERLAP)
+            pipe_prologue<C>(moe_pipe<C, GATE_UP>(a, t, rows_s[0]), lds, nst);
+    }
+    for (int it = 0;; ++it) {
+        const int b = it & 1;
+        const MoeTask t = moe_task(tiles, counts, w, ntn, TN);
+        const int wn = w + slots;
+        Acc<C> r0;
+        if constexpr (OVERLAP) {
+            const Pipe p = moe_pipe<C, GATE_UP>(a, t, rows_s[b]);
+            if (wn < end)
+                rows_dma(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]);
+            leaf_tree_mainloop<C, LOG, false>(p, a.stages_per_leaf, lds, r0);
+            if (wn < end)
+                pipe_prologue<C>(moe_pipe<C, GATE_UP>(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]),
+                                 lds, nst);
+        } else {
+            leaf_tree_mainloop<C, LOG>(moe_pipe<C, GATE_UP>(a, t, rows_s[b]), a.stages_per_leaf,
+                                       lds, r0);
+            if (wn < end)
+                rows_dma(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]);
+        }
+        moe_epilogue<C, GATE_UP>(a, t, r0, rows_s[b], stg);
+        if (wn >= end)
+            break;
+        if constexpr (!OVERLAP)
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // next entries landed
+        w = wn;
     }
 }
 
@@ -371,12 +576,14 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *gate, con
 template <int LOG, bool GU>
 static void launch_expert(const MoeGemmArgs &a, hipStream_t stream)
 {
-    using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
+    // eight waves with a three-stage ring (96 KiB) leave room for the
+    // epilogue's own 32 KiB staging buffer
+    using C = typename std::conditional<(LOG <= 1), CfgDual, TileCfg<4, 3>>::type;
     // resident workgroups, a multiple of 8
     const unsigned grid = static_cast<unsigned>(device_cus() / kXcds * kXcds * (LOG <= 1 ? 2 : 1));
     static_assert(kXcds == 8, "the task split assumes a grid that is a multiple of 8");
     hipLaunchKernelGGL((moe_expert_kernel<C, LOG, GU>), dim3(grid), dim3(C::kThreads), 0, stream,
-                       a);
+                       a, a.tiles, a.counts, a.ntiles);
 }
 
 template <bool GU>
