@@ -11,6 +11,7 @@ comparison kernel and torch's linear layer on the same shape, the
 invariance-sweep shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8
 partitions, the LM-head logprob workload (8192 rows x 2048 x 151936
 vocabulary) in rows/s, the MoE FFN block (4096 tokens, 128 experts, top-8),
+the RMSNorm with residual add in front of the LM-head (8192 x 2048, GB/s),
 plus bitwise invariance checks.  Prints ONE JSON line.
 
 Inputs are seeded synthetic data with the workloads' shapes and
@@ -310,6 +311,28 @@ def main():
                         "tokens_per_s": round(T / (moe_ms * 1e-3), 1),
                         "tflops": round(moe_flop / (moe_ms * 1e-3) / 1e12, 2)}
         del X, lgt, Wg, Wu, Wd, y, wsm, yr
+
+        # ---------------- RMSNorm with residual add in front of the LM-head
+        Mn, Hn = 8192, 2048
+        xn = _dev(normal_bf16(61, (Mn, Hn), 1.0))
+        rn = _dev(normal_bf16(62, (Mn, Hn), 1.0))
+        wn = _dev(normal_bf16(63, (Hn,), 1.0))
+        cn = iso.contract(64, Hn // 64, 0, iso.SCHED_SEQ)
+        yn = torch.empty((Mn, Hn), dtype=torch.bfloat16, device="cuda")
+        ron = torch.empty_like(rn)
+        run_n = lambda: iso.rmsnorm(xn, wn, cn, residual=rn, residual_out=ron, out=yn)
+        run_n()
+        n_ms = _time_events(run_n, max(10, args.steps), stream)
+        y_ref = yn.clone()
+        y1 = iso.rmsnorm(xn[4000:4001].contiguous(), wn, cn, residual=rn[4000:4001].contiguous())
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(y1.view(torch.int16), y_ref[4000:4001].view(torch.int16)))
+        n_bytes = 4 * Mn * Hn * 2 + Hn * 2  # x, residual in; residual, y out; weight
+        extra["rmsnorm"] = {"shape": "8192 x 2048, residual add, 64 leaves of 32, bf16 out",
+                            "us": round(n_ms * 1e3, 2),
+                            "gbs": round(n_bytes / (n_ms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(n_bytes / (n_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del xn, rn, wn, yn, ron, y_ref
 
     extra["bitwise_pass"] = ok
     line["bitwise_pass"] = ok

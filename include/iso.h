@@ -73,6 +73,9 @@ typedef enum iso_status {
 /* schedule: bf16 MFMA 16x16x32 (v_mfma_f32_16x16x32_bf16), FP32 accumulator,
  * K ascending in steps of 32 inside each leaf; the leaf sum starts at +0.0 */
 #define ISO_SCHED_MFMA16X16X32_KASC 1u
+/* schedule: FP32 sum of the leaf's terms one at a time in ascending index
+ * order, starting at +0.0 (reductions that are not matrix products) */
+#define ISO_SCHED_SEQ_KASC 2u
 
 /* Vocabulary chunk width of the LM-head softmax (its leaf size). */
 #define ISO_VOCAB_CHUNK 128u
@@ -85,11 +88,13 @@ typedef enum iso_status {
  *   abi_version  ISO_ABI_VERSION
  *   in_dtype     ISO_BF16 (only)
  *   accum_dtype  ISO_F32 (only)
- *   leaf_count   L: power of two, 1..64
- *   leaf_size    m: multiple of 64, 64..65536; K must equal L * m
+ *   leaf_count   L: power of two, 1..64 (MFMA schedule), 1..4096 (sequential)
+ *   leaf_size    m: multiple of 64, 64..65536 (MFMA schedule), 1..65536
+ *                (sequential); the reduced length (K, H) must equal L * m
  *   tree         ISO_TREE_BALANCED (only)
  *   vocab_chunk  ISO_VOCAB_CHUNK for iso_lmhead_logprob, 0 otherwise
- *   schedule     ISO_SCHED_MFMA16X16X32_KASC (only)
+ *   schedule     ISO_SCHED_MFMA16X16X32_KASC for iso_gemm, iso_lmhead_logprob
+ *                and iso_moe_combine; ISO_SCHED_SEQ_KASC for iso_rmsnorm
  */
 typedef struct iso_contract {
     uint32_t abi_version;
@@ -183,6 +188,35 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
                               const int32_t *tok, float *logprob, int64_t M, int64_t V,
                               int64_t K, int partitions, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/*
+ * Batch-invariant RMSNorm with an optional residual add, the normalization
+ * in front of the LM-head ([KTB] section 4: normalization is one of the
+ * reductions whose order changes a row's bits; section 8: fix the reduction
+ * tree instead of letting the layout choose it).  Per row of H elements:
+ *   h   = bf16(x + residual) when residual != NULL (FP32 add, rounded to
+ *         nearest even), else h = x; residual_out <- h when not NULL;
+ *   ss  = the sum of h_i * h_i over the row: contiguous leaves of
+ *         c->leaf_size elements, each summed one term at a time in ascending
+ *         order in FP32, then the balanced tree over the c->leaf_count leaf
+ *         sums (squares of bf16 values are exact in FP32);
+ *   r   = 1 / sqrt(ss / H + eps), FP32, each operation correctly rounded;
+ *   y_i = (h_i * r) * w_i in FP32, rounded to bf16 (out_dtype ISO_BF16) or
+ *         kept (ISO_F32).
+ * Every step is a correctly rounded FP32 operation in a fixed order, so a
+ * row's bits depend only on that row, and a plain FP32 evaluation in the
+ * same order reproduces them.  c->schedule must be ISO_SCHED_SEQ_KASC and
+ * c->vocab_chunk 0.  Layouts: x, residual, residual_out bf16 [M][H]; weight
+ * bf16 [H]; y [M][H] of out_dtype; all 16-byte aligned.  Limits: H = L * m;
+ * S = H / min(L, 64) is 8, 16, 32, 64 or 128 and S / m is 1, 2, 4 or 8 (a
+ * wave handles a row, each lane one leaf or L/64 whole leaves); M < 2^31;
+ * eps finite and >= 0.  residual_out may alias residual (in place); y must
+ * not alias an input and residual_out must not alias x (ISO_ERR_ARG).
+ * Shape errors give ISO_ERR_SHAPE, a matrix-product contract ISO_ERR_CONTRACT.
+ */
+iso_status iso_rmsnorm(const iso_contract *c, const void *x, const void *residual,
+                       void *residual_out, const void *weight, void *y, uint32_t out_dtype,
+                       int64_t M, int64_t H, float eps, void *stream);
 
 /* Byte offsets of the MoE workspace regions, for inspection of the stages.
  *   idx    int32 [T][top_k]   expert ids in routing order

@@ -55,6 +55,7 @@ def _load():
             "oracle_moe_gate_up": ([P, P, P, P, I64, I64, I64, I64, I, I, P, P], I),
             "oracle_moe_down": ([P, P, P, I64, I64, I64, I64, I, I, P], I),
             "oracle_moe_combine": ([P, P, I64, I64, I, P], I),
+            "oracle_rmsnorm": ([P, P, P, I64, I64, I, ctypes.c_float, I, P, P, P], I),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(lib, name)
@@ -185,3 +186,22 @@ def moe(X, logits, Wg, Wu, Wd, top_k: int, leaves_gate_up: int, leaves_down: int
     e = moe_down(h, Wd, idx, leaves_down)
     y = moe_combine(gate, e)
     return dict(idx=idx, gate=gate, act=act, h=h, e=e, y=y)
+
+
+def rmsnorm(x, w, leaves: int, eps: float, residual=None, out_bf16: bool = True):
+    """RMSNorm of x [M][H] (bf16 bits) with weight w [H]: returns (y, h, ss)
+    with y as bf16 bits (out_bf16) or float32, h = bf16(x + residual) bits
+    (x itself without a residual) and the per-row FP32 sum of squares."""
+    x, w = _u16(x), _u16(w)
+    M, H = x.shape
+    if w.shape != (H,):
+        raise ValueError("w must be [H]")
+    r = None if residual is None else _u16(residual)
+    if r is not None and r.shape != (M, H):
+        raise ValueError("residual must be [M][H]")
+    h = np.empty((M, H), dtype=np.uint16)
+    y = np.empty((M, H), dtype=np.uint16 if out_bf16 else np.float32)
+    ss = np.empty(M, dtype=np.float32)
+    _check(_load().oracle_rmsnorm(_p(x), _p(r), _p(w), M, H, leaves, float(eps),
+                                  1 if out_bf16 else 0, _p(h), _p(y), _p(ss)), "rmsnorm")
+    return y, h, ss

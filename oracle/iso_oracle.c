@@ -51,6 +51,16 @@
  *        decided on the FP32 product silu(G)*U, the precision the kernel takes
  *        that decision in.
  *
+ *  RMSNORM  [KTB] section 4 names normalization among the reductions whose
+ *        order changes a row's result; section 8 fixes the reduction tree.
+ *        The pages give no formula, so the reading is the common RMSNorm
+ *        with a residual add in front: h = bf16(x + r), y_i = h_i /
+ *        sqrt(mean_i(h_i^2) + eps) * w_i.  The sum of squares follows the
+ *        same leaf/tree reading as the GEMM (contiguous leaves, sequential
+ *        FP32 in-leaf sums, balanced tree over the leaves); the mean, the
+ *        square root and the reciprocal are single FP32 operations; the scale
+ *        is applied as (h_i * r) * w_i.
+ *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  * OpenMP splits independent output rows only; no element's order changes.
  * All entry points return 0 on success and -1 on bad arguments.
@@ -404,4 +414,63 @@ int oracle_moe_combine(const double *gate, const float *eout, int64_t T, int64_t
         }
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------- RMSNORM */
+
+/* Per row i of x [M][H] (bf16 bits): h = bf16(x + res) if res, else x
+ * (written to res_out when given); ss = balanced tree over L leaves of
+ * H / L, each the sequential FP32 sum of h_j * h_j; r = 1 / sqrtf(ss / H +
+ * eps); y = (h_j * r) * w_j as float (out_bf16 = 0) or bf16 bits.  ss_out
+ * (may be NULL) receives ss per row. */
+int oracle_rmsnorm(const uint16_t *x, const uint16_t *res, const uint16_t *w, int64_t M,
+                   int64_t H, int L, float eps, int out_bf16, uint16_t *res_out, void *y,
+                   float *ss_out)
+{
+    if (M < 0 || H <= 0 || !is_pow2(L) || H % L != 0 || !x || !w || !y)
+        return -1;
+    const int64_t m = H / L;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t i = 0; i < M; ++i) {
+        float *h = malloc((size_t)H * sizeof(float));
+        float *leaf = malloc((size_t)L * sizeof(float));
+        if (!h || !leaf) {
+            bad = 1;
+            free(h);
+            free(leaf);
+            continue;
+        }
+        for (int64_t j = 0; j < H; ++j) {
+            float v = bf16_bits_to_float(x[i * H + j]);
+            if (res) {
+                uint16_t hb = float_to_bf16_bits(v + bf16_bits_to_float(res[i * H + j]));
+                v = bf16_bits_to_float(hb);
+            }
+            h[j] = v;
+            if (res_out)
+                res_out[i * H + j] = float_to_bf16_bits(v); /* exact: v is a bf16 value */
+        }
+        for (int l = 0; l < L; ++l) {
+            float s = 0.0f;
+            for (int64_t j = l * m; j < (l + 1) * m; ++j)
+                s = s + h[j] * h[j];
+            leaf[l] = s;
+        }
+        const float ss = tree_fold(leaf, L);
+        if (ss_out)
+            ss_out[i] = ss;
+        const float ms = ss / (float)H;
+        const float r = 1.0f / sqrtf(ms + eps);
+        for (int64_t j = 0; j < H; ++j) {
+            const float v = (h[j] * r) * bf16_bits_to_float(w[j]);
+            if (out_bf16)
+                ((uint16_t *)y)[i * H + j] = float_to_bf16_bits(v);
+            else
+                ((float *)y)[i * H + j] = v;
+        }
+        free(h);
+        free(leaf);
+    }
+    return bad ? -1 : 0;
 }

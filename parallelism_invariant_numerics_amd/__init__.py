@@ -41,6 +41,8 @@ lib = ctypes.CDLL(LIB_PATH)
 BF16 = 1
 F32 = 2
 VOCAB_CHUNK = 128
+SCHED_MFMA = 1   # bf16 MFMA 16x16x32 leaves (matrix products)
+SCHED_SEQ = 2    # one term at a time, ascending (RMSNorm)
 _STATUS = {0: "ISO_OK", 1: "ISO_ERR_ARG", 2: "ISO_ERR_SHAPE", 3: "ISO_ERR_DTYPE",
            4: "ISO_ERR_CLAIM", 5: "ISO_ERR_IDENTITY", 6: "ISO_ERR_WORKSPACE",
            7: "ISO_ERR_LAUNCH", 8: "ISO_ERR_CONTRACT"}
@@ -86,6 +88,7 @@ _SIGS = {
     "iso_moe_workspace": ([_I64, _I64, _I64, _I64, _I], ctypes.c_size_t),
     "iso_moe_combine": ([_CP, _CP, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P,
                          ctypes.c_size_t, _P], _I),
+    "iso_rmsnorm": ([_CP, _P, _P, _P, _P, _P, _U32, _I64, _I64, ctypes.c_float, _P], _I),
     "iso_status_str": ([_I], ctypes.c_char_p),
     "iso_version": ([], ctypes.c_char_p),
     "iso_last_launch_error": ([], ctypes.c_char_p),
@@ -107,12 +110,15 @@ def _ok(status: int, where: str):
         raise IsoError(status, where)
 
 
-def contract(leaf_count: int, leaf_size: int, vocab_chunk: int = 0) -> Contract:
+def contract(leaf_count: int, leaf_size: int, vocab_chunk: int = 0,
+             schedule: int = SCHED_MFMA) -> Contract:
     """A validated contract with the library defaults (bf16 in, FP32
-    accumulation, balanced tree, MFMA 16x16x32 schedule)."""
+    accumulation, balanced tree) and the given in-leaf schedule (MFMA for
+    the matrix products, SCHED_SEQ for rmsnorm)."""
     c = Contract()
     _ok(lib.iso_contract_init(ctypes.byref(c), leaf_count, leaf_size, vocab_chunk),
         "iso_contract_init")
+    c.schedule = schedule
     _ok(lib.iso_contract_validate(ctypes.byref(c)), "iso_contract_validate")
     return c
 
@@ -254,6 +260,37 @@ def lmhead_logprob(H, Wvt, tok, c: Contract, *, out=None, partitions: int = 1,
 
 class MoeLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "gate", "h", "e", "total")]
+
+
+def rmsnorm(x, weight, c: Contract, *, residual=None, residual_out=None, eps: float = 1e-6,
+            out=None, out_dtype: int = BF16, stream=None):
+    """y = RMSNorm(x [+ residual]) * weight with the contract's fixed leaf
+    tree over each row.  residual_out (may be `residual` itself) receives
+    bf16(x + residual).  Returns y."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be [M][H]")
+    M, H = x.shape
+    if weight.dim() != 1 or weight.shape[0] != H:
+        raise ValueError("weight must be [H]")
+    for t, name in ((residual, "residual"), (residual_out, "residual_out")):
+        if t is not None and tuple(t.shape) != (M, H):
+            raise ValueError(f"{name} must be [M][H]")
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float32 if out_dtype == F32 else torch.bfloat16,
+                          device=x.device)
+    if out_dtype == F32:
+        optr = _dev_ptr(out, "out", torch.float32)
+    else:
+        optr = _bf16_ptr(out, "out")
+    if tuple(out.shape) != (M, H):
+        raise ValueError("out must be [M][H]")
+    _ok(lib.iso_rmsnorm(ctypes.byref(c), _bf16_ptr(x, "x"),
+                        None if residual is None else _bf16_ptr(residual, "residual"),
+                        None if residual_out is None else _bf16_ptr(residual_out, "residual_out"),
+                        _bf16_ptr(weight, "weight"), optr, out_dtype, M, H, float(eps),
+                        _stream(stream)), "iso_rmsnorm")
+    return out
 
 
 def moe_layout(T: int, H: int, E: int, I: int, top_k: int) -> MoeLayout:

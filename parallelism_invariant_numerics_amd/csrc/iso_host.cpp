@@ -24,12 +24,13 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Contract validity for a region; chunk = the vocab_chunk the region needs.
+// (the matrix-product entry points: MFMA schedule)
 iso_status check_contract(const iso_contract *c, uint32_t chunk)
 {
     iso_status s = iso_contract_validate(c);
     if (s != ISO_OK)
         return s;
-    if (c->vocab_chunk != chunk)
+    if (c->schedule != ISO_SCHED_MFMA16X16X32_KASC || c->vocab_chunk != chunk)
         return ISO_ERR_CONTRACT;
     return ISO_OK;
 }
@@ -120,15 +121,25 @@ iso_status iso_contract_validate(const iso_contract *c)
         return ISO_ERR_CONTRACT;
     if (c->in_dtype != ISO_BF16 || c->accum_dtype != ISO_F32)
         return ISO_ERR_DTYPE;
-    if (!is_pow2(c->leaf_count) || c->leaf_count > 64)
+    if (c->tree != ISO_TREE_BALANCED)
         return ISO_ERR_CONTRACT;
-    if (c->leaf_size < 64 || c->leaf_size > 65536 || c->leaf_size % 64 != 0)
-        return ISO_ERR_CONTRACT;
-    if (c->tree != ISO_TREE_BALANCED || c->schedule != ISO_SCHED_MFMA16X16X32_KASC)
-        return ISO_ERR_CONTRACT;
-    if (c->vocab_chunk != 0 && c->vocab_chunk != ISO_VOCAB_CHUNK)
-        return ISO_ERR_CONTRACT;
-    return ISO_OK;
+    if (c->schedule == ISO_SCHED_MFMA16X16X32_KASC) {
+        if (!is_pow2(c->leaf_count) || c->leaf_count > 64)
+            return ISO_ERR_CONTRACT;
+        if (c->leaf_size < 64 || c->leaf_size > 65536 || c->leaf_size % 64 != 0)
+            return ISO_ERR_CONTRACT;
+        if (c->vocab_chunk != 0 && c->vocab_chunk != ISO_VOCAB_CHUNK)
+            return ISO_ERR_CONTRACT;
+        return ISO_OK;
+    }
+    if (c->schedule == ISO_SCHED_SEQ_KASC) {
+        if (!is_pow2(c->leaf_count) || c->leaf_count > 4096)
+            return ISO_ERR_CONTRACT;
+        if (c->leaf_size < 1 || c->leaf_size > 65536 || c->vocab_chunk != 0)
+            return ISO_ERR_CONTRACT;
+        return ISO_OK;
+    }
+    return ISO_ERR_CONTRACT;
 }
 
 iso_status iso_contract_digest(const iso_contract *c, uint8_t out[32])
@@ -344,6 +355,45 @@ MoeFull moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int top_k)
 
 }  // namespace
 
+iso_status iso_rmsnorm(const iso_contract *c, const void *x, const void *residual,
+                       void *residual_out, const void *weight, void *y, uint32_t out_dtype,
+                       int64_t M, int64_t H, float eps, void *stream)
+{
+    iso_status s = iso_contract_validate(c);
+    if (s != ISO_OK)
+        return s;
+    if (c->schedule != ISO_SCHED_SEQ_KASC)
+        return ISO_ERR_CONTRACT;
+    if (M < 0 || H < 1)
+        return ISO_ERR_ARG;
+    if (H != (int64_t)c->leaf_count * c->leaf_size || H % 8 != 0 || M >= kMaxRows)
+        return ISO_ERR_SHAPE;
+    // one wave per row: each lane holds one leaf, or L/64 whole leaves
+    const int64_t lanes = c->leaf_count < 64 ? (int64_t)c->leaf_count : 64;
+    const int64_t span = H / lanes;  // elements per lane
+    if (span < 8 || span > 128 || !is_pow2(span))
+        return ISO_ERR_SHAPE;
+    if (span % c->leaf_size != 0 || span / c->leaf_size > 8)
+        return ISO_ERR_SHAPE;
+    if (out_dtype != ISO_F32 && out_dtype != ISO_BF16)
+        return ISO_ERR_DTYPE;
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return ISO_ERR_ARG;
+    if (M == 0)
+        return ISO_OK;
+    if (!x || !weight || !y || !aligned16(x) || !aligned16(weight) || !aligned16(y))
+        return ISO_ERR_ARG;
+    if (y == x || y == residual || y == residual_out || residual_out == x)
+        return ISO_ERR_ARG;
+    if ((residual && !aligned16(residual)) || (residual_out && !aligned16(residual_out)))
+        return ISO_ERR_ARG;
+    clear_stale_error();
+    return launch_status(iso::launch_rmsnorm(
+        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(residual),
+        static_cast<uint16_t *>(residual_out), static_cast<const uint16_t *>(weight), y,
+        out_dtype == ISO_BF16 ? 1 : 0, M, H, (int)c->leaf_size, (int)(span / 8), eps,
+        static_cast<hipStream_t>(stream)));
+}
 iso_status iso_moe_layout_of(int64_t T, int64_t H, int64_t E, int64_t I, int top_k,
                              iso_moe_layout *out)
 {

@@ -38,6 +38,11 @@ hipError_t launch_lmhead_finish(const float *ws_stats, const float *ws_target,
                                 const int32_t *tok, float *logprob, int64_t M, int64_t V,
                                 hipStream_t stream);
 
+// RMSNorm rows: leaf_size m, chunks = elements per lane / 8 (1..16).
+hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *residual, uint16_t *residual_out,
+                          const uint16_t *weight, void *y, int out_bf16, int64_t M, int64_t H,
+                          int leaf_size, int chunks, float eps, hipStream_t stream);
+
 struct MoeBuffers {
     int32_t *idx;       // [T][k]
     float *gate;        // [T][k]

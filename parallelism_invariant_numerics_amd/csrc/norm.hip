@@ -1,0 +1,179 @@
+// norm.hip -- batch-invariant RMSNorm with an optional residual add, for
+// gfx950.
+//
+// Normalization is one of the reductions whose order decides a row's bits
+// (katelyatop-blog post on vLLM/SkyRL IsoExec, section 4); the fix is the
+// one of section 8: the contract fixes the reduction tree.  Here the sum of
+// squares of a row is cut into contiguous leaves of m elements, each summed
+// one term at a time in ascending order, and the leaf sums are combined by
+// the balanced binary tree in leaf order.  Nothing in the schedule depends
+// on the number of rows or on a row's position, and every operation is a
+// correctly rounded FP32 operation, so the bits are a function of the row
+// alone and a plain FP32 evaluation in the same order reproduces them.
+//
+// One wave per row.  Lane l holds the row's elements [l S, (l+1) S) with
+// S = 8 NCH: R = S / m whole leaves (R > 1 only when the row has more than
+// 64 leaves), or none when l S >= H (fewer than 64 leaves; those lanes add
+// +0.0, which leaves every tree level above the real leaves unchanged).  The
+// lane's R leaf sums take the lowest log2 R tree levels in registers; the
+// 64 lane roots take the remaining levels across lanes: partners l ^ 1, 2,
+// 4, 8 by DPP row butterflies, then l ^ 16, l ^ 32.  The row is HBM-bound:
+// 16-byte loads and stores, a wave covering S * 64 * 2 contiguous bytes.
+#include "device_common.hpp"
+#include "kernels.h"
+
+namespace iso {
+
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    return static_cast<uint32_t>(f32_to_bf16_rne(lo)) |
+           (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+}
+
+template <int NCH, int R>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict__ x,
+                                                      const uint16_t *res, uint16_t *res_out,
+                                                      const uint16_t *__restrict__ w,
+                                                      void *__restrict__ y, int out_bf16,
+                                                      int64_t M, int64_t H, float eps)
+{
+    constexpr int S = 8 * NCH;  // elements per lane
+    constexpr int LM = S / R;   // leaf size
+    static_assert(S % R == 0, "whole leaves per lane");
+    const int lane = threadIdx.x & 63;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= M)
+        return;  // a whole wave
+    const int64_t c0 = static_cast<int64_t>(lane) * S;
+    const bool active = c0 < H;
+
+    // h = x or bf16(x + residual), two bf16 per word
+    uint32_t h[4 * NCH];
+    if (active) {
+        const u32x4 *xp = reinterpret_cast<const u32x4 *>(x + row * H + c0);
+        u32x4 xv[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            xv[k] = xp[k];
+        if (res) {
+            const u32x4 *rp = reinterpret_cast<const u32x4 *>(res + row * H + c0);
+            u32x4 rv[NCH];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+                rv[k] = rp[k];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    h[4 * k + q] = pack_bf16(bf16_lo(xv[k][q]) + bf16_lo(rv[k][q]),
+                                             bf16_hi(xv[k][q]) + bf16_hi(rv[k][q]));
+        } else {
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    h[4 * k + q] = xv[k][q];
+        }
+        if (res_out) {
+            u32x4 *op = reinterpret_cast<u32x4 *>(res_out + row * H + c0);
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)
+                op[k] = u32x4{h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4 * NCH; ++q)
+            h[q] = 0u;
+    }
+
+    // leaf sums (one term at a time, ascending), then the lane's subtree
+    float leaf[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = r * LM; i < (r + 1) * LM; ++i) {
+            const float v = (i & 1) ? bf16_hi(h[i >> 1]) : bf16_lo(h[i >> 1]);
+            s = s + v * v;
+        }
+        leaf[r] = s;
+    }
+#pragma unroll
+    for (int width = R; width > 1; width >>= 1)
+#pragma unroll
+        for (int q = 0; q < width / 2; ++q)
+            leaf[q] = leaf[2 * q] + leaf[2 * q + 1];
+    float ss = row16_sum(leaf[0]);
+    ss = ss + shfl_xor(ss, 16);
+    ss = ss + shfl_xor(ss, 32);
+
+    const float ms = ss / static_cast<float>(H);
+    const float rs = 1.0f / sqrtf(ms + eps);
+
+    if (!active)
+        return;
+    const u32x4 *wp = reinterpret_cast<const u32x4 *>(w + c0);
+    if (out_bf16) {
+        u32x4 *op = reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + row * H + c0);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const u32x4 wv = wp[k];
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pack_bf16((bf16_lo(h[4 * k + q]) * rs) * bf16_lo(wv[q]),
+                                 (bf16_hi(h[4 * k + q]) * rs) * bf16_hi(wv[q]));
+            op[k] = o;
+        }
+    } else {
+        f32x4 *op = reinterpret_cast<f32x4 *>(static_cast<float *>(y) + row * H + c0);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const u32x4 wv = wp[k];
+#pragma unroll
+            for (int q = 0; q < 4; q += 2)
+                op[2 * k + q / 2] = f32x4{(bf16_lo(h[4 * k + q]) * rs) * bf16_lo(wv[q]),
+                                          (bf16_hi(h[4 * k + q]) * rs) * bf16_hi(wv[q]),
+                                          (bf16_lo(h[4 * k + q + 1]) * rs) * bf16_lo(wv[q + 1]),
+                                          (bf16_hi(h[4 * k + q + 1]) * rs) * bf16_hi(wv[q + 1])};
+        }
+    }
+}
+
+template <int NCH>
+static hipError_t launch_norm_r(int R, const uint16_t *x, const uint16_t *residual,
+                                uint16_t *residual_out, const uint16_t *weight, void *y,
+                                int out_bf16, int64_t M, int64_t H, float eps, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>((M + 3) / 4));
+    switch (R) {
+    case 1: hipLaunchKernelGGL((rmsnorm_kernel<NCH, 1>), grid, dim3(256), 0, stream, x, residual, residual_out, weight, y, out_bf16, M, H, eps); break;
+    case 2: hipLaunchKernelGGL((rmsnorm_kernel<NCH, 2>), grid, dim3(256), 0, stream, x, residual, residual_out, weight, y, out_bf16, M, H, eps); break;
+    case 4: hipLaunchKernelGGL((rmsnorm_kernel<NCH, 4>), grid, dim3(256), 0, stream, x, residual, residual_out, weight, y, out_bf16, M, H, eps); break;
+    case 8: hipLaunchKernelGGL((rmsnorm_kernel<NCH, 8>), grid, dim3(256), 0, stream, x, residual, residual_out, weight, y, out_bf16, M, H, eps); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *residual, uint16_t *residual_out,
+                          const uint16_t *weight, void *y, int out_bf16, int64_t M, int64_t H,
+                          int leaf_size, int chunks, float eps, hipStream_t stream)
+{
+    const int span = 8 * chunks;
+    if (leaf_size <= 0 || span % leaf_size != 0)
+        return hipErrorInvalidValue;
+    const int R = span / leaf_size;
+    switch (chunks) {
+    case 1: return launch_norm_r<1>(R, x, residual, residual_out, weight, y, out_bf16, M, H, eps, stream);
+    case 2: return launch_norm_r<2>(R, x, residual, residual_out, weight, y, out_bf16, M, H, eps, stream);
+    case 4: return launch_norm_r<4>(R, x, residual, residual_out, weight, y, out_bf16, M, H, eps, stream);
+    case 8: return launch_norm_r<8>(R, x, residual, residual_out, weight, y, out_bf16, M, H, eps, stream);
+    case 16: return launch_norm_r<16>(R, x, residual, residual_out, weight, y, out_bf16, M, H, eps, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace iso

@@ -81,3 +81,21 @@ def tree_case_inputs(pin, leaf_size: int, rows: int = 1, cols: int = 1, kind=Non
 
 def f32_bits(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float32).view(np.uint32)
+
+
+def rmsnorm_pins():
+    """Rows of rmsnorm_pins.txt grouped by kind."""
+    out = {"ss": [], "add": [], "y": []}
+    for row in _lines("rmsnorm_pins.txt"):
+        kind = row[0]
+        if kind == "ss":
+            out["ss"].append(dict(H=int(row[1]), L=int(row[2]),
+                                  h=[int(v, 16) for v in row[3].split()],
+                                  expected=int(row[4], 16)))
+        elif kind == "add":
+            out["add"].append(dict(x=int(row[1], 16), r=int(row[2], 16), h=int(row[3], 16)))
+        elif kind == "y":
+            out["y"].append(dict(H=int(row[1]), L=int(row[2]), h=int(row[3], 16),
+                                 w=int(row[4], 16), eps=float(row[5]),
+                                 y_bf16=int(row[6], 16), y_f32=int(row[7], 16)))
+    return out

@@ -182,3 +182,39 @@ def test_moe_rejections_before_launch():
     lay = iso.moe_layout(16, 256, 8, 128, 4)
     assert lay.idx < lay.gate < lay.h < lay.e < lay.total == need
     assert lay.e - lay.h >= 16 * 4 * 128 * 2 and lay.total - lay.e >= 16 * 4 * 256 * 4
+
+
+def _norm(c, M=4, H=2048, x=FAKE, r=None, ro=None, w=FAKE + 0x100000, y=FAKE + 0x200000,
+          od=iso.BF16, eps=1e-6):
+    return iso.lib.iso_rmsnorm(ctypes.byref(c), x, r, ro, w, y, od, M, H, eps, None)
+
+
+def test_rmsnorm_rejections_before_launch():
+    c = iso.contract(64, 32, 0, iso.SCHED_SEQ)
+    assert _norm(iso.contract(8, 256, 0)) == 8          # a matrix-product contract
+    assert _norm(c, H=1024) == 2                        # H != L * m
+    assert _norm(c, M=-1) == 1
+    assert _norm(c, od=7) == 3
+    assert _norm(c, eps=-1.0) == 1 and _norm(c, eps=float("nan")) == 1
+    assert _norm(c, x=None) == 1 and _norm(c, w=None) == 1
+    assert _norm(c, x=FAKE + 2) == 1                    # 16-byte alignment
+    assert _norm(c, y=FAKE) == 1                        # y aliases x
+    assert _norm(c, r=FAKE + 0x300000, ro=FAKE) == 1    # residual_out aliases x
+    assert _norm(c, M=0) == 0                           # empty: nothing launched
+    wide = iso.contract(64, 256, 0, iso.SCHED_SEQ)      # 256 elements per lane
+    assert _norm(wide, H=16384) == 2
+    many = iso.contract(4096, 1, 0, iso.SCHED_SEQ)      # 64 leaves per lane
+    assert _norm(many, H=4096) == 2
+    few = iso.contract(8, 4, 0, iso.SCHED_SEQ)          # 4 elements per lane
+    assert _norm(few, H=32) == 2
+
+
+def test_sequential_schedule_contracts():
+    c = iso.contract(64, 32, 0, iso.SCHED_SEQ)
+    assert iso.digest(c) == hashlib.sha256(_canonical(c)).digest()
+    assert iso.digest(c) != iso.digest(iso.contract(64, 32 * 64, 0))
+    for L, m, chunk in [(3, 32, 0), (8192, 1, 0), (64, 0, 0), (64, 32, 128)]:
+        bad = _raw(leaf_count=L, leaf_size=m, vocab_chunk=chunk, schedule=iso.SCHED_SEQ)
+        assert iso.lib.iso_contract_validate(ctypes.byref(bad)) == 8
+    # the matrix products refuse a sequential-schedule contract
+    assert _gemm(iso.contract(8, 256, 0, iso.SCHED_SEQ)) == 8
