@@ -282,6 +282,34 @@ def main():
                            "ms": round(lm_ms, 4),
                            "tflops": round(lm_flop / (lm_ms * 1e-3) / 1e12, 2),
                            "mfma_frac": round(lm_flop / (lm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        # the same layer split over 8 vocabulary shards (stats exchange + final tree)
+        nch = (lm["V"] + 127) // 128
+        st8 = torch.empty((lm["M"], nch, 2), dtype=torch.float32, device="cuda")
+        tg8 = torch.empty(lm["M"], dtype=torch.float32, device="cuda")
+        cuts = [round(i * nch / 8) * 128 for i in range(8)] + [lm["V"]]
+
+        def run_sh():
+            for i in range(8):
+                iso.lmhead_shard_stats(H, Wv[cuts[i]:cuts[i + 1]], tok, cl, lm["V"], cuts[i],
+                                       st8, tg8)
+            return iso.lmhead_finish(st8, tg8, tok, lm["V"], out=lp8s)
+        lp8s = torch.empty_like(lp_ref)
+        run_sh()
+        sh_ms = _time_events(run_sh, max(3, args.steps // 10), stream)
+        ok &= bool(torch.equal(lp8s.view(torch.int32), lp_ref.view(torch.int32)))
+        extra["lmhead"]["vocab_shards8_ms"] = round(sh_ms, 4)
+        # decode: one row per call (weights streamed from HBM every step)
+        lp1 = torch.empty(1, dtype=torch.float32, device="cuda")
+        ws1 = torch.empty(iso.lmhead_workspace(cl, 1, lm["V"], 1), dtype=torch.uint8,
+                          device="cuda")
+        H1, tok1 = H[:1].contiguous(), tok[:1].contiguous()
+        run_d = lambda: iso.lmhead_logprob(H1, Wv, tok1, cl, out=lp1, workspace=ws1)
+        run_d()
+        d_ms = _time_events(run_d, max(10, args.steps), stream)
+        ok &= bool(torch.equal(lp1.view(torch.int32), lp_ref[:1].view(torch.int32)))
+        extra["decode"] = {"lmhead_1row_us": round(d_ms * 1e3, 2),
+                           "lmhead_1row_weight_gbs": round(lm["V"] * lm["K"] * 2 / (d_ms * 1e-3) / 1e9, 1)}
+        del st8, tg8, lp8s, lp1, ws1
         del H, Wv, tok, lp, wsl
 
         # ---------------- MoE FFN block with the routing-order combine

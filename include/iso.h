@@ -190,6 +190,31 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
                               size_t workspace_bytes, void *stream);
 
 /*
+ * The vocabulary-sharded LM-head, split at its exchange point (one GPU
+ * stands in for the ranks of a vocabulary-parallel layer; [AGL] "Achieving
+ * Parallelism Invariance": partials are combined by the fixed tree whatever
+ * the layout).  A shard owns the whole chunks of token ids [v_begin, v_end)
+ * of a V-token vocabulary (v_begin a multiple of ISO_VOCAB_CHUNK; v_end too,
+ * or v_end = V) and Wvt_shard points at row v_begin of Wvt [V][K].
+ * iso_lmhead_shard_stats writes, for each row r and each chunk c of the
+ * shard, stats[r][c][0] = the chunk max and stats[r][c][1] = the chunk's
+ * exp-sum tree (both FP32, stats is [M][ceil(V / 128)][2]), and target[r] =
+ * the FP32 logit of tok[r] when tok[r] lies in the shard.  Once every shard
+ * has written (in any order: the writes are disjoint), iso_lmhead_finish
+ * folds each row's chunk pairs over the balanced tree in chunk order and
+ * gives the same logprob bits as iso_lmhead_logprob (NaN for a token id
+ * outside [0, V)).  The contract is the iso_lmhead_logprob one, with at most
+ * 16 leaves (the per-shard kernel runs one partition).  Buffers are the
+ * caller's, device memory; a row's stats come only from its own data.
+ */
+iso_status iso_lmhead_shard_stats(const iso_contract *c, const void *H, const void *Wvt_shard,
+                                  const int32_t *tok, float *stats, float *target, int64_t M,
+                                  int64_t V, int64_t v_begin, int64_t v_end, int64_t K,
+                                  void *stream);
+iso_status iso_lmhead_finish(const float *stats, const float *target, const int32_t *tok,
+                             float *logprob, int64_t M, int64_t V, void *stream);
+
+/*
  * Batch-invariant RMSNorm with an optional residual add, the normalization
  * in front of the LM-head ([KTB] section 4: normalization is one of the
  * reductions whose order changes a row's bits; section 8: fix the reduction

@@ -89,6 +89,8 @@ _SIGS = {
     "iso_moe_combine": ([_CP, _CP, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P,
                          ctypes.c_size_t, _P], _I),
     "iso_rmsnorm": ([_CP, _P, _P, _P, _P, _P, _U32, _I64, _I64, ctypes.c_float, _P], _I),
+    "iso_lmhead_shard_stats": ([_CP, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], _I),
+    "iso_lmhead_finish": ([_P, _P, _P, _P, _I64, _I64, _P], _I),
     "iso_status_str": ([_I], ctypes.c_char_p),
     "iso_version": ([], ctypes.c_char_p),
     "iso_last_launch_error": ([], ctypes.c_char_p),
@@ -260,6 +262,36 @@ def lmhead_logprob(H, Wvt, tok, c: Contract, *, out=None, partitions: int = 1,
 
 class MoeLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("idx", "gate", "h", "e", "total")]
+
+
+def lmhead_shard_stats(H, Wvt_shard, tok, c: Contract, V: int, v_begin: int, stats, target, *,
+                       stream=None):
+    """Chunk statistics of the vocabulary shard [v_begin, v_begin + rows of
+    Wvt_shard) into the shared stats [M][ceil(V/128)][2] and target [M]
+    buffers (float32 device tensors)."""
+    torch = _torch()
+    M, K = H.shape
+    v_end = v_begin + Wvt_shard.shape[0]
+    _ok(lib.iso_lmhead_shard_stats(ctypes.byref(c), _bf16_ptr(H, "H"),
+                                   _bf16_ptr(Wvt_shard, "Wvt_shard"),
+                                   _dev_ptr(tok, "tok", torch.int32),
+                                   _dev_ptr(stats, "stats", torch.float32),
+                                   _dev_ptr(target, "target", torch.float32), M, V, v_begin,
+                                   v_end, K, _stream(stream)), "iso_lmhead_shard_stats")
+
+
+def lmhead_finish(stats, target, tok, V: int, *, out=None, stream=None):
+    """logprob [M] from the gathered chunk statistics of every shard."""
+    torch = _torch()
+    M = tok.shape[0]
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=tok.device)
+    _ok(lib.iso_lmhead_finish(_dev_ptr(stats, "stats", torch.float32),
+                              _dev_ptr(target, "target", torch.float32),
+                              _dev_ptr(tok, "tok", torch.int32),
+                              _dev_ptr(out, "out", torch.float32), M, V, _stream(stream)),
+        "iso_lmhead_finish")
+    return out
 
 
 def rmsnorm(x, weight, c: Contract, *, residual=None, residual_out=None, eps: float = 1e-6,

@@ -299,12 +299,57 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
     float *roots = parts > 1 ? reinterpret_cast<float *>(ws + l.roots) : nullptr;
     hipError_t e = iso::launch_lmhead_stats(
         static_cast<const uint16_t *>(H), static_cast<const uint16_t *>(Wvt), tok, stats, target,
-        roots, M, V, K, (int)c->leaf_count / parts, (int)c->leaf_size, parts, st);
+        roots, M, V, K, (int)c->leaf_count / parts, (int)c->leaf_size, parts, 0, V, st);
     if (e != hipSuccess)
         return launch_status(e);
     return launch_status(iso::launch_lmhead_finish(stats, target, tok, logprob, M, V, st));
 }
 
+iso_status iso_lmhead_shard_stats(const iso_contract *c, const void *H, const void *Wvt_shard,
+                                  const int32_t *tok, float *stats, float *target, int64_t M,
+                                  int64_t V, int64_t v_begin, int64_t v_end, int64_t K,
+                                  void *stream)
+{
+    iso_status s = check_contract(c, ISO_VOCAB_CHUNK);
+    if (s != ISO_OK)
+        return s;
+    if (V < 1 || V > kMaxVocab)
+        return ISO_ERR_SHAPE;
+    if (v_begin < 0 || v_end <= v_begin || v_end > V || v_begin % ISO_VOCAB_CHUNK != 0 ||
+        (v_end != V && v_end % ISO_VOCAB_CHUNK != 0))
+        return ISO_ERR_SHAPE;  // whole chunks, the last one may be ragged at V
+    const int64_t Vs = v_end - v_begin;
+    if ((s = check_gemm_shape(c, M, Vs, K)) != ISO_OK)
+        return s;
+    if (((M + 127) / 128) * ((Vs + 127) / 128) >= ((int64_t)1 << 31))
+        return ISO_ERR_SHAPE;
+    if ((int)c->leaf_count > kMaxLeavesPerTile)
+        return ISO_ERR_CLAIM;  // one partition: the register tree holds at most 16 leaves
+    if (M == 0)
+        return ISO_OK;
+    if (!H || !Wvt_shard || !tok || !stats || !target || !aligned16(H) || !aligned16(Wvt_shard))
+        return ISO_ERR_ARG;
+    clear_stale_error();
+    return launch_status(iso::launch_lmhead_stats(
+        static_cast<const uint16_t *>(H), static_cast<const uint16_t *>(Wvt_shard), tok, stats,
+        target, nullptr, M, Vs, K, (int)c->leaf_count, (int)c->leaf_size, 1, v_begin, V,
+        static_cast<hipStream_t>(stream)));
+}
+iso_status iso_lmhead_finish(const float *stats, const float *target, const int32_t *tok,
+                             float *logprob, int64_t M, int64_t V, void *stream)
+{
+    if (M < 0 || V < 1)
+        return ISO_ERR_ARG;
+    if (V > kMaxVocab || M >= kMaxRows)
+        return ISO_ERR_SHAPE;
+    if (M == 0)
+        return ISO_OK;
+    if (!stats || !target || !tok || !logprob)
+        return ISO_ERR_ARG;
+    clear_stale_error();
+    return launch_status(
+        iso::launch_lmhead_finish(stats, target, tok, logprob, M, V, static_cast<hipStream_t>(stream)));
+}
 namespace {
 
 struct MoeFull {

@@ -28,10 +28,13 @@ hipError_t launch_partition_combine(const float *ws, void *out, int out_bf16, in
 // exp-sum) and the target logit ws_target [M].  parts == 1 fuses the stats
 // into the leaf/tree main loop; parts > 1 first writes partition roots of the
 // logits to ws_roots [parts][M][V].
+// Chunk statistics of the vocabulary ids [v0, v0 + V) (Wvt points at row v0
+// of the vocabulary matrix; v0 a multiple of 128) of a v_total vocabulary:
+// stats rows have stride ceil(v_total / 128) chunks.
 hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int32_t *tok,
                                float *ws_stats, float *ws_target, float *ws_roots, int64_t M,
                                int64_t V, int64_t K, int leaves_per_part, int leaf_size,
-                               int parts, hipStream_t stream);
+                               int parts, int64_t v0, int64_t v_total, hipStream_t stream);
 
 // Per row: fixed tree over the chunk statistics, then the logprob.
 hipError_t launch_lmhead_finish(const float *ws_stats, const float *ws_target,

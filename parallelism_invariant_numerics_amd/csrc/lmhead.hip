@@ -33,10 +33,13 @@ struct LmArgs {
     const uint16_t *H;
     const uint16_t *Wvt;
     const int32_t *tok;
-    float *stats;   // [M][nchunk][2]
+    float *stats;   // [M][stats_stride][2]
     float *target;  // [M]
     const float *roots;  // [parts][M][V] (several partitions only)
-    int64_t M, V, K, nchunk;
+    int64_t M, V, K, nchunk;  // V, nchunk: this call's vocabulary (a shard or all of it)
+    int64_t v0;               // first token id of this call's vocabulary
+    int64_t chunk0;           // its first chunk in the whole vocabulary
+    int64_t stats_stride;     // chunks of the whole vocabulary (stats row stride)
     int stages_per_leaf;
 };
 
@@ -134,7 +137,7 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
 #pragma unroll
                     for (int q = 1; q < C::WC; ++q)
                         cm = fmaxf(cm, red_m[q * 128 + rt]);
-                    float *st = a.stats + (row * a.nchunk + chunk) * 2;
+                    float *st = a.stats + (row * a.stats_stride + a.chunk0 + chunk) * 2;
                     st[0] = cm;
                     st[1] = tree_waves<C>(red_s, rt);
                 }
@@ -151,7 +154,7 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
             const int64_t row = m0 + rt;
             if (row >= a.M)
                 continue;
-            const int64_t t = tok_s[rt];
+            const int64_t t = tok_s[rt] - a.v0;  // token id within this call's vocabulary
             const int64_t rel = t - n0 - wc * WCOLS - (lane & 15);
             if (rel >= 0 && rel < WCOLS && (rel & 15) == 0 && t < a.V) {
                 const int j = static_cast<int>(rel >> 4);
@@ -356,7 +359,7 @@ static hipError_t launch_fused(const LmArgs &a, hipStream_t stream)
 hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int32_t *tok,
                                float *ws_stats, float *ws_target, float *ws_roots, int64_t M,
                                int64_t V, int64_t K, int leaves_per_part, int leaf_size,
-                               int parts, hipStream_t stream)
+                               int parts, int64_t v0, int64_t v_total, hipStream_t stream)
 {
     LmArgs a;
     a.H = H;
@@ -369,6 +372,9 @@ hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int
     a.V = V;
     a.K = K;
     a.nchunk = (V + kChunk - 1) / kChunk;
+    a.v0 = v0;
+    a.chunk0 = v0 / kChunk;
+    a.stats_stride = (v_total + kChunk - 1) / kChunk;
     a.stages_per_leaf = leaf_size / BK;
     if (parts == 1) {
         switch (leaves_per_part) {

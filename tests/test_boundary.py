@@ -218,3 +218,27 @@ def test_sequential_schedule_contracts():
         assert iso.lib.iso_contract_validate(ctypes.byref(bad)) == 8
     # the matrix products refuse a sequential-schedule contract
     assert _gemm(iso.contract(8, 256, 0, iso.SCHED_SEQ)) == 8
+
+
+def _shard(c, M=4, V=1000, vb=0, ve=512, K=1024, H=FAKE, W=FAKE, tok=FAKE, st=FAKE, tg=FAKE):
+    return iso.lib.iso_lmhead_shard_stats(ctypes.byref(c), H, W, tok, st, tg, M, V, vb, ve, K,
+                                          None)
+
+
+def test_lmhead_shard_rejections_before_launch():
+    c = iso.contract(8, 128, 128)
+    assert _shard(c, vb=100) == 2                  # shard start inside a chunk
+    assert _shard(c, ve=600) == 2                  # shard end inside a chunk, not at V
+    assert _shard(c, ve=1001) == 2                 # past the vocabulary
+    assert _shard(c, vb=512, ve=512) == 2          # empty shard
+    assert _shard(c, K=512) == 2                   # K != L * m
+    assert _shard(iso.contract(8, 128, 0)) == 8    # not a logprob contract
+    assert _shard(iso.contract(32, 64, 128), K=2048) == 4  # deeper than one register tree
+    assert _shard(c, tok=None) == 1 and _shard(c, W=FAKE + 2) == 1
+    assert _shard(c, vb=512, ve=1000, M=0) == 0    # empty: nothing launched
+    fin = iso.lib.iso_lmhead_finish
+    assert fin(FAKE, FAKE, FAKE, FAKE, -1, 100, None) == 1
+    assert fin(FAKE, FAKE, FAKE, FAKE, 4, 0, None) == 1
+    assert fin(FAKE, FAKE, FAKE, FAKE, 4, (1 << 20) + 1, None) == 2
+    assert fin(None, FAKE, FAKE, FAKE, 4, 100, None) == 1
+    assert fin(FAKE, FAKE, FAKE, FAKE, 0, 100, None) == 0
