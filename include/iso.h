@@ -138,6 +138,72 @@ iso_status iso_contract_check(const iso_contract *c, const uint8_t want[32]);
  */
 iso_status iso_check_partitions(const iso_contract *c, int partitions);
 
+/* ---------------------------------------------------------------- identities
+ * [AGL] "Contract Structure and Enforcement": an execution contract splits
+ * the forward operators into regions (arithmetic spans implemented by one
+ * kernel) and cases (such as engine_prefill and trainer_fwd) saying how each
+ * region runs; each (region, case) pair pins a composition (accumulation
+ * dtype, reduction decomposition); claims list the partition counts for which
+ * the tree is proven not to change the bits; SHA-256 identities named
+ * semantic, numerical_policy and deployment let two runtimes check that they
+ * run the same verified policy.  [KTB] section 6: a model checksum plus a
+ * numerical-execution checksum, checked like a lockfile.
+ */
+
+/* SHA-256 over any bytes, fed in pieces.  The semantic identity is this
+ * digest over the model's weights and configuration, in an order the caller
+ * fixes.  Errors: ISO_ERR_ARG for NULL (update accepts n == 0 with NULL). */
+typedef struct iso_sha256 {
+    uint32_t h[8];
+    uint64_t nbytes;
+    uint8_t buf[64];
+    uint32_t nbuf;
+} iso_sha256;
+iso_status iso_sha256_init(iso_sha256 *s);
+iso_status iso_sha256_update(iso_sha256 *s, const void *data, size_t n);
+iso_status iso_sha256_final(iso_sha256 *s, uint8_t out[32]);
+
+/* One (region, case) composition of an execution contract.
+ *   region, case_name  NUL-terminated ASCII names of 1..31 characters
+ *                      (bytes after the NUL are ignored)
+ *   policy             the region's contract, as passed to its entry point
+ *   partitions         the partition count this case runs the region with
+ *   claims             bit k set: partition count 2^k (k = 0..3) is claimed
+ *                      not to change the region's bits; every claimed count
+ *                      must divide the policy's leaf count (MFMA schedule)
+ *                      or be 1 (sequential schedule) */
+typedef struct iso_composition {
+    char region[32];
+    char case_name[32];
+    iso_contract policy;
+    uint32_t partitions;
+    uint32_t claims;
+} iso_composition;
+
+/* numerical_policy and deployment identities of a table of n compositions
+ * (each (region, case) at most once; the table's order does not matter):
+ *   numerical_policy = SHA-256 of the 30-byte tag
+ *       "iso.numerical_policy.table.v1\0", n as uint32 LE, then for every
+ *       composition in (region, case_name) byte order: region and case_name
+ *       zero-padded to 32 bytes each, the 8 policy fields and claims as
+ *       uint32 LE;
+ *   deployment = SHA-256 of the 18-byte tag "iso.deployment.v1\0",
+ *       iso_version() zero-padded to 32 bytes, n as uint32 LE, then for
+ *       every composition in the same order: region[32], case_name[32],
+ *       partitions as uint32 LE.
+ * Errors: ISO_ERR_ARG for NULL, a bad name or a repeated (region, case); a
+ * malformed policy's own code; ISO_ERR_CLAIM when partitions is not claimed
+ * or a claim is not a valid split of the policy. */
+iso_status iso_table_digests(const iso_composition *table, size_t n,
+                             uint8_t numerical_policy[32], uint8_t deployment[32]);
+
+/* The per-call check before a launch: the (region, case) composition must be
+ * in the table (ISO_ERR_ARG otherwise), `c` must have its policy's
+ * numerical_policy digest (ISO_ERR_IDENTITY), and `partitions` must be
+ * among its claims (ISO_ERR_CLAIM). */
+iso_status iso_table_check(const iso_composition *table, size_t n, const char *region,
+                           const char *case_name, const iso_contract *c, int partitions);
+
 /* Workspace bytes iso_gemm needs for this shape (0 when none); (size_t)-1
  * for arguments iso_gemm would reject. */
 size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int partitions);

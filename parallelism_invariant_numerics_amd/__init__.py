@@ -67,6 +67,18 @@ class IsoError(RuntimeError):
         super().__init__(f"{where}: {self.name} ({msg})")
 
 
+class Sha256State(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_uint32 * 8), ("nbytes", ctypes.c_uint64),
+                ("buf", ctypes.c_uint8 * 64), ("nbuf", ctypes.c_uint32)]
+
+
+class Composition(ctypes.Structure):
+    """One (region, case) composition of an execution contract."""
+    _fields_ = [("region", ctypes.c_char * 32), ("case_name", ctypes.c_char * 32),
+                ("policy", Contract), ("partitions", ctypes.c_uint32),
+                ("claims", ctypes.c_uint32)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I = ctypes.c_int
@@ -91,6 +103,13 @@ _SIGS = {
     "iso_rmsnorm": ([_CP, _P, _P, _P, _P, _P, _U32, _I64, _I64, ctypes.c_float, _P], _I),
     "iso_lmhead_shard_stats": ([_CP, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], _I),
     "iso_lmhead_finish": ([_P, _P, _P, _P, _I64, _I64, _P], _I),
+    "iso_sha256_init": ([ctypes.POINTER(Sha256State)], _I),
+    "iso_sha256_update": ([ctypes.POINTER(Sha256State), _P, ctypes.c_size_t], _I),
+    "iso_sha256_final": ([ctypes.POINTER(Sha256State), ctypes.c_char_p], _I),
+    "iso_table_digests": ([ctypes.POINTER(Composition), ctypes.c_size_t, ctypes.c_char_p,
+                           ctypes.c_char_p], _I),
+    "iso_table_check": ([ctypes.POINTER(Composition), ctypes.c_size_t, ctypes.c_char_p,
+                         ctypes.c_char_p, _CP, _I], _I),
     "iso_status_str": ([_I], ctypes.c_char_p),
     "iso_version": ([], ctypes.c_char_p),
     "iso_last_launch_error": ([], ctypes.c_char_p),
@@ -377,3 +396,60 @@ def moe_stages(workspace, T: int, H: int, E: int, I: int, top_k: int) -> dict:
                 gate=view(lay.gate, tk, torch.float32, (T, top_k)),
                 h=view(lay.h, tk * I, torch.bfloat16, (T, top_k, I)),
                 e=view(lay.e, tk * H, torch.float32, (T, top_k, H)))
+
+
+# ------------------------------------------------------------------ identities
+
+def semantic_digest(items) -> bytes:
+    """SHA-256 over the bytes of `items` in order: numpy arrays and torch
+    tensors (copied to the host, contiguous, raw element bytes), bytes, or
+    str (UTF-8, e.g. a model configuration as canonical JSON)."""
+    import numpy as np
+    st = Sha256State()
+    _ok(lib.iso_sha256_init(ctypes.byref(st)), "iso_sha256_init")
+    for it in items:
+        if isinstance(it, str):
+            buf = it.encode()
+        elif isinstance(it, (bytes, bytearray)):
+            buf = bytes(it)
+        elif hasattr(it, "detach"):  # torch tensor
+            t = it.detach().contiguous().cpu()
+            buf = t.view(_torch().uint8).numpy().tobytes() if t.numel() else b""
+        else:
+            buf = np.ascontiguousarray(it).tobytes()
+        _ok(lib.iso_sha256_update(ctypes.byref(st), buf, len(buf)), "iso_sha256_update")
+    out = ctypes.create_string_buffer(32)
+    _ok(lib.iso_sha256_final(ctypes.byref(st), out), "iso_sha256_final")
+    return out.raw
+
+
+class ExecutionContract:
+    """Regions x cases compositions with their identities, and the per-call
+    check.  compositions: {(region, case): (contract, partitions, claims)}
+    where claims is an iterable of partition counts."""
+
+    def __init__(self, compositions: dict, semantic: bytes = b""):
+        self._table = (Composition * len(compositions))()
+        for i, ((region, case), (c, p, claims)) in enumerate(sorted(compositions.items())):
+            e = self._table[i]
+            e.region = region.encode()
+            e.case_name = case.encode()
+            e.policy = c
+            e.partitions = p
+            e.claims = sum(1 << (int(q).bit_length() - 1) for q in set(claims))
+        self.semantic = semantic
+        pol = ctypes.create_string_buffer(32)
+        dep = ctypes.create_string_buffer(32)
+        _ok(lib.iso_table_digests(self._table, len(compositions), pol, dep), "iso_table_digests")
+        self.numerical_policy = pol.raw
+        self.deployment = dep.raw
+
+    def identities(self) -> dict:
+        return {"semantic": self.semantic, "numerical_policy": self.numerical_policy,
+                "deployment": self.deployment}
+
+    def check(self, region: str, case: str, c: Contract, partitions: int = 1) -> None:
+        """Raises IsoError (ISO_ERR_IDENTITY / ISO_ERR_CLAIM / ISO_ERR_ARG)
+        unless the call matches the registered composition."""
+        _ok(lib.iso_table_check(self._table, len(self._table), region.encode(), case.encode(),
+                                ctypes.byref(c), partitions), "iso_table_check")

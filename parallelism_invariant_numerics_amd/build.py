@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["gemm.hip", "lmhead.hip", "moe.hip", "norm.hip"]
-HOST_SOURCES = ["iso_host.cpp", "sha256.cpp"]
+HOST_SOURCES = ["iso_host.cpp", "sha256.cpp", "identity.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++20", "-Wall", "-I", os.path.join(ROOT, "include")]
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-ffp-contract=off", "-fno-fast-math",

@@ -61,23 +61,47 @@ void compress(uint32_t h[8], const uint8_t block[64])
 
 }  // namespace
 
-void sha256(const uint8_t *msg, size_t len, uint8_t out[32])
+void Sha256::reset()
 {
-    uint32_t h[8] = {0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53au,
-                     0x510e527fu, 0x9b05688cu, 0x1f83d9abu, 0x5be0cd19u};
-    size_t done = 0;
-    while (len - done >= 64) {
-        compress(h, msg + done);
-        done += 64;
+    static const uint32_t kInit[8] = {0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53au,
+                                      0x510e527fu, 0x9b05688cu, 0x1f83d9abu, 0x5be0cd19u};
+    memcpy(h, kInit, sizeof h);
+    nbytes = 0;
+    nbuf = 0;
+}
+
+void Sha256::update(const uint8_t *msg, size_t len)
+{
+    nbytes += len;
+    if (nbuf > 0) {
+        const size_t take = len < 64 - nbuf ? len : 64 - nbuf;
+        memcpy(buf + nbuf, msg, take);
+        nbuf += (uint32_t)take;
+        msg += take;
+        len -= take;
+        if (nbuf < 64)
+            return;
+        compress(h, buf);
+        nbuf = 0;
     }
+    while (len >= 64) {
+        compress(h, msg);
+        msg += 64;
+        len -= 64;
+    }
+    memcpy(buf, msg, len);
+    nbuf = (uint32_t)len;
+}
+
+void Sha256::finish(uint8_t out[32])
+{
     // padding: 0x80, zeros, then the bit length as a 64-bit big-endian integer
     uint8_t tail[128];
-    size_t rem = len - done;
     memset(tail, 0, sizeof tail);
-    memcpy(tail, msg + done, rem);
-    tail[rem] = 0x80;
-    size_t tail_len = (rem + 1 + 8 <= 64) ? 64 : 128;
-    uint64_t bits = (uint64_t)len * 8u;
+    memcpy(tail, buf, nbuf);
+    tail[nbuf] = 0x80;
+    const size_t tail_len = (nbuf + 1 + 8 <= 64) ? 64 : 128;
+    const uint64_t bits = nbytes * 8u;
     for (int i = 0; i < 8; ++i)
         tail[tail_len - 1 - i] = (uint8_t)(bits >> (8 * i));
     compress(h, tail);
@@ -89,6 +113,14 @@ void sha256(const uint8_t *msg, size_t len, uint8_t out[32])
         out[4 * i + 2] = (uint8_t)(h[i] >> 8);
         out[4 * i + 3] = (uint8_t)h[i];
     }
+}
+
+void sha256(const uint8_t *msg, size_t len, uint8_t out[32])
+{
+    Sha256 s;
+    s.reset();
+    s.update(msg, len);
+    s.finish(out);
 }
 
 }  // namespace iso
