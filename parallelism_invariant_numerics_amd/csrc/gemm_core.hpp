@@ -306,6 +306,14 @@ __device__ __forceinline__ void pipe_prologue(const Pipe &p, char *lds, int nst)
 // may be reused by the caller.  Global stores or loads that the caller has in
 // flight only make the ring's vmcnt waits stricter (loads complete in order,
 // so "at most n outstanding" still implies that the oldest stage landed).
+//
+// A buffer load holds up the wave that issues it until the address unit has
+// taken it, and that unit is shared by the CU.  Waves w and w + 4 of an
+// eight-wave workgroup share a SIMD, so the upper four waves issue their
+// loads of the stage after their first k-step's MFMAs instead of right after
+// the barrier: while one wave of a SIMD waits on the address unit, the other
+// one keeps the matrix core busy.  The loads still go out before the next
+// stage's wait, so the ring's counts are unchanged.
 template <class C, int LOG, bool PROLOGUE = true>
 __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char *lds,
                                                    Acc<C> &root)
@@ -317,6 +325,7 @@ __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave / C::WC;
     const int wc = wave % C::WC;
+    const bool late = C::kWaves == 8 && wave >= 4;
 
     const uint32_t lds_addr = (uint32_t)(uintptr_t)(ISO_LDS char *)lds;
     const uint32_t ch0 = (uint32_t)(((lane >> 4) ^ (lane & 7)) << 4);
@@ -345,7 +354,8 @@ __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char 
             frag_wait(f1);  // previous stage's reads done before its buffer is recycled
             const int ahead = nst - 1 - st;
             stage_barrier<C>(ahead < NB - 2 ? ahead : NB - 2);
-            if (st + NB - 1 < nst)
+            const bool dma = st + NB - 1 < nst;
+            if (dma && !late)
                 stage_dma<C>(p, lds, st + NB - 1, (st + NB - 1) % NB);
             const uint32_t base = lds_addr + (uint32_t)(st % NB) * kStageBytes;
             frag_read(f0, base + rowa + ch0, base + rowb + ch0);
@@ -358,6 +368,8 @@ __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char 
                     }
                 }
             }
+            if (dma && late)
+                stage_dma<C>(p, lds, st + NB - 1, (st + NB - 1) % NB);
             frag_wait(f0);
             frag_read(f1, base + rowa + ch1, base + rowb + ch1);
             mfma_step(acc, f0);
