@@ -26,6 +26,9 @@ __all__ = [
     "normal_f32",
     "CONFIGS",
     "make_config",
+    "unit_rows_bf16",
+    "uniform_f32",
+    "cpr_inputs",
 ]
 
 _BLOCK = 1 << 24  # elements per draw block
@@ -122,3 +125,34 @@ def make_config(name: str, rows: int | None = None) -> dict:
                    ordering_seed=s[5])
         return out
     raise KeyError(name)
+
+
+def unit_rows_bf16(seed: int, shape) -> np.ndarray:
+    """N(0, 1) draws, each last-axis row scaled to unit L2 norm in float64,
+    then rounded to bf16 (the normalised query/key rows a linear-attention
+    layer feeds its recurrence)."""
+    shape = tuple(int(s) for s in shape)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape)
+    x = x / np.linalg.norm(x, axis=-1, keepdims=True)
+    return f32_to_bf16_bits(x.astype(np.float32))
+
+
+def uniform_f32(seed: int, shape, lo: float, hi: float) -> np.ndarray:
+    """U[lo, hi) float32 samples."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(lo, hi, size=tuple(int(s) for s in shape)).astype(np.float32)
+
+
+def cpr_inputs(T: int, H: int, d: int, seed: int = 601) -> dict:
+    """One gated-delta-rule layer's per-token inputs for T tokens and H heads of
+    size d: q, k unit rows [T][H][d] (bf16 bits), v ~ N(0, 1) [T][H][d] (bf16
+    bits), decay gate alpha ~ U[0.9, 1) and write strength beta ~ U[0, 1)
+    [T][H] float32.  Seeds seed .. seed + 4."""
+    return {
+        "q": unit_rows_bf16(seed, (T, H, d)),
+        "k": unit_rows_bf16(seed + 1, (T, H, d)),
+        "v": normal_bf16(seed + 2, (T, H, d), 1.0),
+        "alpha": uniform_f32(seed + 3, (T, H), 0.9, 1.0),
+        "beta": uniform_f32(seed + 4, (T, H), 0.0, 1.0),
+    }

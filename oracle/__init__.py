@@ -56,6 +56,9 @@ def _load():
             "oracle_moe_down": ([P, P, P, I64, I64, I64, I64, I, I, P], I),
             "oracle_moe_combine": ([P, P, I64, I64, I, P], I),
             "oracle_rmsnorm": ([P, P, P, I64, I64, I, ctypes.c_float, I, P, P, P], I),
+            "oracle_cpr_prefill": ([P, P, P, P, P, P, I64, I64, I, I, P, P, P, P], I),
+            "oracle_cpr_decode_step": ([P, P, P, P, P, I64, I64, I, I, P, P, P], I),
+            "oracle_cpr_transition": ([P, P, P, P, I, I, P, P], I),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(lib, name)
@@ -205,3 +208,67 @@ def rmsnorm(x, w, leaves: int, eps: float, residual=None, out_bf16: bool = True)
     _check(_load().oracle_rmsnorm(_p(x), _p(r), _p(w), M, H, leaves, float(eps),
                                   1 if out_bf16 else 0, _p(h), _p(y), _p(ss)), "rmsnorm")
     return y, h, ss
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError("expected float32")
+    return a
+
+
+def _cpr_inputs(q, k, v, alpha, beta):
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    alpha, beta = _f32(alpha), _f32(beta)
+    if q.ndim != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must be [T][H][d]")
+    T, H, d = q.shape
+    if alpha.shape != (T, H) or beta.shape != (T, H):
+        raise ValueError("alpha, beta must be [T][H]")
+    return q, k, v, alpha, beta, T, H, d
+
+
+def cpr_prefill(q, k, v, alpha, beta, chunk: int, S0=None, bounds: bool = False):
+    """CPR Gated DeltaNet prefill of q, k, v [T][H][d] (bf16 bits), alpha,
+    beta [T][H] float32, from boundary state S0 [H][d][d] (zeros if None).
+    Returns (o [T][H][d], snap [H][d][d], run [H][d][d]) and, with
+    bounds=True, every boundary state [T//chunk + 1][H][d][d] as well."""
+    q, k, v, alpha, beta, T, H, d = _cpr_inputs(q, k, v, alpha, beta)
+    if S0 is not None:
+        S0 = _f32(S0)
+        if S0.shape != (H, d, d):
+            raise ValueError("S0 must be [H][d][d]")
+    o = np.empty((T, H, d), np.float32)
+    snap = np.empty((H, d, d), np.float32)
+    run = np.empty((H, d, d), np.float32)
+    bnd = np.empty((T // chunk + 1, H, d, d), np.float32) if bounds else None
+    _check(_load().oracle_cpr_prefill(_p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(S0), T, H, d,
+                                      chunk, _p(o), _p(snap), _p(run), _p(bnd)), "cpr_prefill")
+    return (o, snap, run, bnd) if bounds else (o, snap, run)
+
+
+def cpr_decode_step(q, k, v, alpha, beta, chunk: int, pos: int, snap, run):
+    """One CPR decode step for token `pos` of the [T][H][d] history arrays;
+    returns (o [H][d], snap, run) with the states updated (copies)."""
+    q, k, v, alpha, beta, T, H, d = _cpr_inputs(q, k, v, alpha, beta)
+    if not 0 <= pos < T:
+        raise ValueError("pos outside the history")
+    snap = _f32(snap).copy()
+    run = _f32(run).copy()
+    o = np.empty((H, d), np.float32)
+    _check(_load().oracle_cpr_decode_step(_p(q), _p(k), _p(v), _p(alpha), _p(beta), pos, H, d,
+                                          chunk, _p(snap), _p(run), _p(o)), "cpr_decode_step")
+    return o, snap, run
+
+
+def cpr_transition(k, v, alpha, beta):
+    """Chunk form (P, U) [d][d] of n tokens of one head: k, v [n][d] bf16
+    bits, alpha, beta [n] float32."""
+    k, v = _u16(k), _u16(v)
+    alpha, beta = _f32(alpha), _f32(beta)
+    n, d = k.shape
+    P = np.empty((d, d), np.float32)
+    U = np.empty((d, d), np.float32)
+    _check(_load().oracle_cpr_transition(_p(k), _p(v), _p(alpha), _p(beta), n, d, _p(P), _p(U)),
+           "cpr_transition")
+    return P, U

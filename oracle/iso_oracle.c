@@ -61,6 +61,29 @@
  *        square root and the reciprocal are single FP32 operations; the scale
  *        is applied as (h_i * r) * w_i.
  *
+ *  CPR   [AGL] "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet" and [KTB]
+ *        sections 10-11: the recurrence is the primary numerical definition,
+ *        evaluated in parallel across chunks, and decode re-synchronises the
+ *        hidden state every C tokens (C = chunk size), so trainer, prefill and
+ *        decode agree bit for bit.  The pages give no GDN equations; the reading
+ *        is the gated delta rule with a d x d state S (row a = value index,
+ *        column j = key index) per head:
+ *            S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *            o_t = S_t q_t,
+ *        one token "step" evaluated as u = S k, w = beta (v - alpha u),
+ *        S <- alpha S + w k^T, o = S q, each dot product a balanced binary tree
+ *        over the d products in index order, every other operation a single
+ *        FP32 multiply or add in the order written.  CPR reading: inside chunk
+ *        c every output comes from steps started at the chunk's boundary state
+ *        B_c; the next boundary state is not the stepped state but the chunk
+ *        form of the same map, B_{c+1} = B_c P_c + U_c with P_c = A_0 ... A_{C-1}
+ *        (A_i = alpha_i (I - beta_i k_i k_i^T)) and U_c = sum_i beta_i v_i k_i^T
+ *        A_{i+1} ... A_{C-1}, both built by a backward scan over the chunk that
+ *        needs no state; the pass B_c -> B_{c+1} is a d x d x d product with
+ *        tree-ordered sums.  A decode step is the same token step on the
+ *        running state; when a token closes a chunk the running state is
+ *        replaced by B_{c+1} from the same chunk form (the re-sync).
+ *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  * OpenMP splits independent output rows only; no element's order changes.
  * All entry points return 0 on success and -1 on bad arguments.
@@ -473,4 +496,240 @@ int oracle_rmsnorm(const uint16_t *x, const uint16_t *res, const uint16_t *w, in
         free(leaf);
     }
     return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ CPR */
+
+/* Balanced binary tree over x[0..d) * y[0..d) (d a power of two), products
+ * rounded first, then pairs (2i, 2i+1) at every level. */
+static float tree_dot(const float *x, const float *y, int d, float *tmp)
+{
+    for (int j = 0; j < d; ++j)
+        tmp[j] = x[j] * y[j];
+    return tree_fold(tmp, d);
+}
+
+/* One token of the gated delta rule on S [d][d]; writes o [d]. */
+static void cpr_step(float *S, const float *q, const float *k, const float *v, float alpha,
+                     float beta, int d, float *o, float *tmp)
+{
+    for (int a = 0; a < d; ++a) {
+        float *row = S + (int64_t)a * d;
+        const float u = tree_dot(row, k, d, tmp);
+        const float w = beta * (v[a] - alpha * u);
+        for (int j = 0; j < d; ++j)
+            row[j] = alpha * row[j] + w * k[j];
+        o[a] = tree_dot(row, q, d, tmp);
+    }
+}
+
+/* Chunk form of n tokens (k, v [n][d] widened, alpha, beta [n]): the backward
+ * scan R <- A_i R from R = I, U <- U + beta_i v_i (k_i^T R) before each update. */
+static void cpr_transition(const float *k, const float *v, const float *alpha, const float *beta,
+                           int n, int d, float *P, float *U, float *r, float *col, float *tmp)
+{
+    for (int m = 0; m < d; ++m)
+        for (int j = 0; j < d; ++j)
+            P[(int64_t)m * d + j] = m == j ? 1.0f : 0.0f;
+    memset(U, 0, (size_t)d * d * sizeof(float));
+    for (int i = n - 1; i >= 0; --i) {
+        const float *ki = k + (int64_t)i * d, *vi = v + (int64_t)i * d;
+        for (int j = 0; j < d; ++j) {
+            for (int m = 0; m < d; ++m)
+                col[m] = P[(int64_t)m * d + j];
+            r[j] = tree_dot(ki, col, d, tmp);
+        }
+        for (int a = 0; a < d; ++a) {
+            const float t = beta[i] * vi[a];
+            for (int j = 0; j < d; ++j)
+                U[(int64_t)a * d + j] = U[(int64_t)a * d + j] + t * r[j];
+        }
+        for (int m = 0; m < d; ++m) {
+            const float sm = beta[i] * ki[m];
+            for (int j = 0; j < d; ++j)
+                P[(int64_t)m * d + j] = alpha[i] * (P[(int64_t)m * d + j] - sm * r[j]);
+        }
+    }
+}
+
+/* B_next = U + B P, every entry's sum over m a balanced tree. */
+static void cpr_pass(const float *B, const float *P, const float *U, int d, float *Bn, float *col,
+                     float *tmp)
+{
+    for (int j = 0; j < d; ++j) {
+        for (int m = 0; m < d; ++m)
+            col[m] = P[(int64_t)m * d + j];
+        for (int a = 0; a < d; ++a)
+            Bn[(int64_t)a * d + j] = U[(int64_t)a * d + j] + tree_dot(B + (int64_t)a * d, col, d, tmp);
+    }
+}
+
+static void widen(const uint16_t *src, int64_t stride, int d, float *dst)
+{
+    for (int j = 0; j < d; ++j)
+        dst[j] = bf16_bits_to_float(src[(int64_t)j * stride]);
+    (void)stride;
+}
+
+/* Per-head scratch for the CPR entry points. */
+struct cpr_scratch {
+    float *q, *k, *v, *al, *be, *P, *U, *r, *col, *tmp, *o;
+};
+static int cpr_scratch_alloc(struct cpr_scratch *w, int C, int d)
+{
+    w->q = malloc((size_t)d * sizeof(float));
+    w->k = malloc((size_t)C * d * sizeof(float));
+    w->v = malloc((size_t)C * d * sizeof(float));
+    w->al = malloc((size_t)C * sizeof(float));
+    w->be = malloc((size_t)C * sizeof(float));
+    w->P = malloc((size_t)d * d * sizeof(float));
+    w->U = malloc((size_t)d * d * sizeof(float));
+    w->r = malloc((size_t)d * sizeof(float));
+    w->col = malloc((size_t)d * sizeof(float));
+    w->tmp = malloc((size_t)d * sizeof(float));
+    w->o = malloc((size_t)d * sizeof(float));
+    return w->q && w->k && w->v && w->al && w->be && w->P && w->U && w->r && w->col && w->tmp && w->o;
+}
+static void cpr_scratch_free(struct cpr_scratch *w)
+{
+    free(w->q); free(w->k); free(w->v); free(w->al); free(w->be); free(w->P);
+    free(w->U); free(w->r); free(w->col); free(w->tmp); free(w->o);
+}
+
+/* Token t of head h from [T][H][d] bf16 arrays, widened into k/v slot `slot`. */
+static void cpr_load(const uint16_t *k, const uint16_t *v, const float *alpha, const float *beta,
+                     int64_t H, int d, int64_t t, int64_t h, struct cpr_scratch *w, int slot)
+{
+    widen(k + (t * H + h) * d, 1, d, w->k + (int64_t)slot * d);
+    widen(v + (t * H + h) * d, 1, d, w->v + (int64_t)slot * d);
+    w->al[slot] = alpha[t * H + h];
+    w->be[slot] = beta[t * H + h];
+}
+
+/*
+ * Prefill of T tokens, H heads, head size d (a power of two), chunk C.
+ *   q, k, v    [T][H][d] bf16 bits;  alpha, beta [T][H] FP32
+ *   S0         [H][d][d] initial boundary state, or NULL for zeros
+ *   o          [T][H][d] FP32 outputs
+ *   snap       [H][d][d] the boundary state at the last chunk boundary <= T
+ *   run        [H][d][d] the state a decode step continues from: the
+ *              boundary state when T is a multiple of C, else the stepped
+ *              state after token T-1
+ *   bounds     optional [T/C + 1][H][d][d]: every boundary state B_0 .. B_{T/C}
+ */
+int oracle_cpr_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
+                       const float *beta, const float *S0, int64_t T, int64_t H, int d, int C,
+                       float *o, float *snap, float *run, float *bounds)
+{
+    if (T < 0 || H <= 0 || !is_pow2(d) || C <= 0 || !q || !k || !v || !alpha || !beta || !o ||
+        !snap || !run)
+        return -1;
+    const int64_t dd = (int64_t)d * d;
+    const int64_t nb = T / C;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (int64_t h = 0; h < H; ++h) {
+        struct cpr_scratch w;
+        float *B = malloc((size_t)dd * sizeof(float));
+        float *Bn = malloc((size_t)dd * sizeof(float));
+        float *S = malloc((size_t)dd * sizeof(float));
+        if (!cpr_scratch_alloc(&w, C, d) || !B || !Bn || !S) {
+            bad = 1;
+            cpr_scratch_free(&w); free(B); free(Bn); free(S);
+            continue;
+        }
+        if (S0)
+            memcpy(B, S0 + h * dd, (size_t)dd * sizeof(float));
+        else
+            memset(B, 0, (size_t)dd * sizeof(float));
+        if (bounds)
+            memcpy(bounds + h * dd, B, (size_t)dd * sizeof(float));
+        for (int64_t c0 = 0; c0 < T; c0 += C) {
+            const int n = (int)(T - c0 < C ? T - c0 : C);
+            memcpy(S, B, (size_t)dd * sizeof(float));
+            for (int i = 0; i < n; ++i) {
+                const int64_t t = c0 + i;
+                cpr_load(k, v, alpha, beta, H, d, t, h, &w, i);
+                widen(q + (t * H + h) * d, 1, d, w.q);
+                cpr_step(S, w.q, w.k + (int64_t)i * d, w.v + (int64_t)i * d, w.al[i], w.be[i], d,
+                         o + (t * H + h) * d, w.tmp);
+            }
+            if (n == C) {
+                cpr_transition(w.k, w.v, w.al, w.be, n, d, w.P, w.U, w.r, w.col, w.tmp);
+                cpr_pass(B, w.P, w.U, d, Bn, w.col, w.tmp);
+                memcpy(B, Bn, (size_t)dd * sizeof(float));
+                if (bounds)
+                    memcpy(bounds + ((c0 / C + 1) * H + h) * dd, B, (size_t)dd * sizeof(float));
+            }
+        }
+        memcpy(snap + h * dd, B, (size_t)dd * sizeof(float));
+        memcpy(run + h * dd, (T % C == 0) ? B : S, (size_t)dd * sizeof(float));
+        cpr_scratch_free(&w); free(B); free(Bn); free(S);
+    }
+    (void)nb;
+    return bad ? -1 : 0;
+}
+
+/*
+ * One decode step: token `pos` (q, k, v, alpha, beta hold tokens 0..pos in the
+ * prefill layout), snap/run [H][d][d] in/out, o [H][d].  When pos closes a
+ * chunk, snap and run both become the next boundary state (the re-sync).
+ */
+int oracle_cpr_decode_step(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const float *alpha, const float *beta, int64_t pos, int64_t H, int d,
+                           int C, float *snap, float *run, float *o)
+{
+    if (pos < 0 || H <= 0 || !is_pow2(d) || C <= 0 || !q || !k || !v || !alpha || !beta || !snap ||
+        !run || !o)
+        return -1;
+    const int64_t dd = (int64_t)d * d;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t h = 0; h < H; ++h) {
+        struct cpr_scratch w;
+        float *Bn = malloc((size_t)dd * sizeof(float));
+        if (!cpr_scratch_alloc(&w, C, d) || !Bn) {
+            bad = 1;
+            cpr_scratch_free(&w); free(Bn);
+            continue;
+        }
+        const int slot = (int)(pos % C);
+        cpr_load(k, v, alpha, beta, H, d, pos, h, &w, slot);
+        widen(q + (pos * H + h) * d, 1, d, w.q);
+        cpr_step(run + h * dd, w.q, w.k + (int64_t)slot * d, w.v + (int64_t)slot * d, w.al[slot],
+                 w.be[slot], d, o + h * d, w.tmp);
+        if (slot == C - 1) {
+            for (int i = 0; i < C; ++i)
+                cpr_load(k, v, alpha, beta, H, d, pos - (C - 1) + i, h, &w, i);
+            cpr_transition(w.k, w.v, w.al, w.be, C, d, w.P, w.U, w.r, w.col, w.tmp);
+            cpr_pass(snap + h * dd, w.P, w.U, d, Bn, w.col, w.tmp);
+            memcpy(snap + h * dd, Bn, (size_t)dd * sizeof(float));
+            memcpy(run + h * dd, Bn, (size_t)dd * sizeof(float));
+        }
+        cpr_scratch_free(&w); free(Bn);
+    }
+    return bad ? -1 : 0;
+}
+
+/* The chunk form alone, for pins: P, U [d][d] of n tokens of one head
+ * (k, v [n][d] bf16 bits, alpha, beta [n]). */
+int oracle_cpr_transition(const uint16_t *k, const uint16_t *v, const float *alpha,
+                          const float *beta, int n, int d, float *P, float *U)
+{
+    if (n <= 0 || !is_pow2(d) || !k || !v || !alpha || !beta || !P || !U)
+        return -1;
+    struct cpr_scratch w;
+    if (!cpr_scratch_alloc(&w, n, d)) {
+        cpr_scratch_free(&w);
+        return -1;
+    }
+    for (int i = 0; i < n; ++i) {
+        widen(k + (int64_t)i * d, 1, d, w.k + (int64_t)i * d);
+        widen(v + (int64_t)i * d, 1, d, w.v + (int64_t)i * d);
+        w.al[i] = alpha[i];
+        w.be[i] = beta[i];
+    }
+    cpr_transition(w.k, w.v, w.al, w.be, n, d, P, U, w.r, w.col, w.tmp);
+    cpr_scratch_free(&w);
+    return 0;
 }

@@ -99,3 +99,20 @@ def rmsnorm_pins():
                                  w=int(row[4], 16), eps=float(row[5]),
                                  y_bf16=int(row[6], 16), y_f32=int(row[7], 16)))
     return out
+
+
+def cpr_pins():
+    """The hand-worked CPR example of cpr_pins.txt: B0 [2][2], tokens as
+    (k, v, q, alpha, beta), outputs o [3][2], the chunk form (P, U) of the
+    first chunk, and the final snap / run states."""
+    out = {"tok": [], "o": None}
+    for row in _lines("cpr_pins.txt"):
+        kind = row[0]
+        nums = [[float(x) for x in f.split()] for f in row[1:]]
+        if kind == "tok":
+            out["tok"].append(dict(k=nums[0], v=nums[1], q=nums[2], alpha=nums[3][0], beta=nums[4][0]))
+        elif kind == "o":
+            out["o"] = nums
+        else:
+            out[kind] = nums[0]
+    return out
