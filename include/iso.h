@@ -76,6 +76,11 @@ typedef enum iso_status {
 /* schedule: FP32 sum of the leaf's terms one at a time in ascending index
  * order, starting at +0.0 (reductions that are not matrix products) */
 #define ISO_SCHED_SEQ_KASC 2u
+/* schedule: CPR gated delta rule (iso_cpr_prefill, iso_cpr_decode_step):
+ * leaf_count = head size d (the dot products are balanced trees over d
+ * single-product leaves), leaf_size = chunk length C (the state re-sync
+ * interval), every operation a single FP32 multiply or add */
+#define ISO_SCHED_CPR_GDN 3u
 
 /* Vocabulary chunk width of the LM-head softmax (its leaf size). */
 #define ISO_VOCAB_CHUNK 128u
@@ -94,7 +99,9 @@ typedef enum iso_status {
  *   tree         ISO_TREE_BALANCED (only)
  *   vocab_chunk  ISO_VOCAB_CHUNK for iso_lmhead_logprob, 0 otherwise
  *   schedule     ISO_SCHED_MFMA16X16X32_KASC for iso_gemm, iso_lmhead_logprob
- *                and iso_moe_combine; ISO_SCHED_SEQ_KASC for iso_rmsnorm
+ *                and iso_moe_combine; ISO_SCHED_SEQ_KASC for iso_rmsnorm;
+ *                ISO_SCHED_CPR_GDN for the CPR entry points (leaf_count = d,
+ *                a power of two up to 4096; leaf_size = C, 1..64)
  */
 typedef struct iso_contract {
     uint32_t abi_version;
@@ -308,6 +315,64 @@ iso_status iso_lmhead_finish(const float *stats, const float *target, const int3
 iso_status iso_rmsnorm(const iso_contract *c, const void *x, const void *residual,
                        void *residual_out, const void *weight, void *y, uint32_t out_dtype,
                        int64_t M, int64_t H, float eps, void *stream);
+
+/*
+ * CPR gated delta rule ([AGL] "Chunkwise-Parallel Recurrent (CPR) Gated
+ * DeltaNet"; [KTB] sections 10-11): the recurrence is the numerical
+ * definition, evaluated in parallel across chunks, and decode re-syncs the
+ * state every C tokens so that prefill and decode give the same bits.  The
+ * pages give no equations; the rule is, per head with a d x d FP32 state S
+ * (row a = value index, column j = key index),
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * one token step being u = S k, w = beta (v - alpha u), S <- alpha S + w k^T,
+ * o = S q (dot products: balanced trees over the d products in index order;
+ * every other operation one FP32 multiply or add, no contraction).  Inside
+ * chunk c the outputs are token steps from the chunk's boundary state B_c;
+ * the next boundary is B_{c+1} = U_c + B_c P_c, with (P_c, U_c) the chunk
+ * form of the same map (backward scan R = I, U = 0; for i = C-1 .. 0:
+ * r = k_i^T R, U <- U + (beta_i v_i) r, R <- alpha_i (R - (beta_i k_i) r);
+ * P_c = R), not the stepped state.
+ *
+ * Contract: schedule ISO_SCHED_CPR_GDN, leaf_count = d (this build: 128),
+ * leaf_size = C (1..64), vocab_chunk 0 (else ISO_ERR_CONTRACT; d != 128 is
+ * ISO_ERR_SHAPE).  Layouts: q, k, v bf16 [T][H][d]; alpha, beta FP32
+ * [T][H]; states FP32 [H][d][d] row-major; all 16-byte aligned.
+ * Limits: 1 <= H < 65536, 0 <= T, ceil(T / C) < 65536.
+ */
+
+/* Workspace bytes iso_cpr_prefill needs for T tokens (pass T = C for
+ * iso_cpr_decode_step); (size_t)-1 for arguments the calls would reject. */
+size_t iso_cpr_workspace(const iso_contract *c, int64_t H, int64_t T);
+
+/*
+ * Prefill of T tokens from the boundary state S0 (NULL: zeros):
+ *   o     FP32 [T][H][d]  outputs
+ *   snap  FP32 [H][d][d]  B_{floor(T/C)}, the last boundary state
+ *   run   FP32 [H][d][d]  the state the next decode step continues from:
+ *                         snap when T is a multiple of C, else the stepped
+ *                         state after token T-1
+ * S0 may alias snap; snap and run must differ and o must not alias an input
+ * (ISO_ERR_ARG).
+ */
+iso_status iso_cpr_prefill(const iso_contract *c, const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, const float *S0, float *o,
+                           float *snap, float *run, int64_t T, int64_t H, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step of token `pos` for every head.  q, k, v, alpha, beta are
+ * the sequence arrays of the prefill layout holding tokens 0..pos (token pos
+ * just appended); snap and run (FP32 [H][d][d], distinct) are updated in
+ * place and o (FP32 [H][d]) receives the outputs.  When pos + 1 is a multiple
+ * of C the step also re-syncs: snap and run become B_{(pos+1)/C} from the
+ * chunk form of tokens pos-C+1 .. pos, which gives the same bits as a
+ * prefill through pos.  Workspace: iso_cpr_workspace(c, H, C) bytes.
+ */
+iso_status iso_cpr_decode_step(const iso_contract *c, const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta, int64_t pos, float *snap,
+                               float *run, float *o, int64_t H, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /* Byte offsets of the MoE workspace regions, for inspection of the stages.
  *   idx    int32 [T][top_k]   expert ids in routing order

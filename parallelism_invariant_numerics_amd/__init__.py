@@ -25,6 +25,7 @@ __all__ = [
     "IsoError", "Contract", "contract", "digest", "check_identity", "check_partitions",
     "gemm_workspace", "gemm", "gemm_baseline", "lmhead_workspace", "lmhead_logprob",
     "moe_workspace", "moe_layout", "moe_combine", "moe_stages",
+    "cpr_contract", "cpr_workspace", "cpr_prefill", "cpr_decode_step",
     "lib", "LIB_PATH", "F32", "BF16", "VOCAB_CHUNK", "version",
 ]
 
@@ -43,6 +44,7 @@ F32 = 2
 VOCAB_CHUNK = 128
 SCHED_MFMA = 1   # bf16 MFMA 16x16x32 leaves (matrix products)
 SCHED_SEQ = 2    # one term at a time, ascending (RMSNorm)
+SCHED_CPR = 3    # CPR gated delta rule: leaf_count = head size, leaf_size = chunk
 _STATUS = {0: "ISO_OK", 1: "ISO_ERR_ARG", 2: "ISO_ERR_SHAPE", 3: "ISO_ERR_DTYPE",
            4: "ISO_ERR_CLAIM", 5: "ISO_ERR_IDENTITY", 6: "ISO_ERR_WORKSPACE",
            7: "ISO_ERR_LAUNCH", 8: "ISO_ERR_CONTRACT"}
@@ -101,6 +103,11 @@ _SIGS = {
     "iso_moe_combine": ([_CP, _CP, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P,
                          ctypes.c_size_t, _P], _I),
     "iso_rmsnorm": ([_CP, _P, _P, _P, _P, _P, _U32, _I64, _I64, ctypes.c_float, _P], _I),
+    "iso_cpr_workspace": ([_CP, _I64, _I64], ctypes.c_size_t),
+    "iso_cpr_prefill": ([_CP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, ctypes.c_size_t,
+                         _P], _I),
+    "iso_cpr_decode_step": ([_CP, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _I64, _P,
+                             ctypes.c_size_t, _P], _I),
     "iso_lmhead_shard_stats": ([_CP, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], _I),
     "iso_lmhead_finish": ([_P, _P, _P, _P, _I64, _I64, _P], _I),
     "iso_sha256_init": ([ctypes.POINTER(Sha256State)], _I),
@@ -341,6 +348,90 @@ def rmsnorm(x, weight, c: Contract, *, residual=None, residual_out=None, eps: fl
                         None if residual_out is None else _bf16_ptr(residual_out, "residual_out"),
                         _bf16_ptr(weight, "weight"), optr, out_dtype, M, H, float(eps),
                         _stream(stream)), "iso_rmsnorm")
+    return out
+
+
+def cpr_contract(chunk: int, head_size: int = 128) -> Contract:
+    """Contract of the CPR gated delta rule: head size d (tree leaves of the
+    dot products) and chunk length C (the state re-sync interval)."""
+    return contract(head_size, chunk, 0, SCHED_CPR)
+
+
+def cpr_workspace(c: Contract, H: int, T: int) -> int:
+    n = lib.iso_cpr_workspace(ctypes.byref(c), H, T)
+    if n == _BAD_SIZE:
+        raise IsoError(1, "iso_cpr_workspace")
+    return n
+
+
+def _cpr_seq(q, k, v, alpha, beta):
+    if q.dim() != 3 or tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError("q, k, v must be [T][H][d]")
+    T, H, _ = q.shape
+    if tuple(alpha.shape) != (T, H) or tuple(beta.shape) != (T, H):
+        raise ValueError("alpha, beta must be [T][H]")
+    return T, H
+
+
+def cpr_prefill(q, k, v, alpha, beta, c: Contract, *, S0=None, out=None, snap=None, run=None,
+                workspace=None, stream=None):
+    """CPR prefill of q, k, v [T][H][d] (bf16), alpha, beta [T][H] (float32)
+    from the boundary state S0 [H][d][d] (zeros if None).  Returns
+    (o [T][H][d], snap [H][d][d], run [H][d][d]) as float32 tensors."""
+    torch = _torch()
+    T, H = _cpr_seq(q, k, v, alpha, beta)
+    d = q.shape[2]
+    dev = q.device
+    if S0 is not None and tuple(S0.shape) != (H, d, d):
+        raise ValueError("S0 must be [H][d][d]")
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    if snap is None:
+        snap = torch.empty((H, d, d), dtype=torch.float32, device=dev)
+    if run is None:
+        run = torch.empty((H, d, d), dtype=torch.float32, device=dev)
+    if workspace is None:
+        ws, wsb = _workspace(cpr_workspace(c, H, T), dev, None)
+    else:  # the entry point checks its size
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    _ok(lib.iso_cpr_prefill(ctypes.byref(c), _bf16_ptr(q, "q"), _bf16_ptr(k, "k"),
+                            _bf16_ptr(v, "v"), _dev_ptr(alpha, "alpha", torch.float32),
+                            _dev_ptr(beta, "beta", torch.float32),
+                            None if S0 is None else _dev_ptr(S0, "S0", torch.float32),
+                            _dev_ptr(out, "out", torch.float32),
+                            _dev_ptr(snap, "snap", torch.float32),
+                            _dev_ptr(run, "run", torch.float32), T, H,
+                            None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
+        "iso_cpr_prefill")
+    return out, snap, run
+
+
+def cpr_decode_step(q, k, v, alpha, beta, pos: int, snap, run, c: Contract, *, out=None,
+                    workspace=None, stream=None):
+    """One CPR decode step of token `pos` of the sequence arrays (tokens
+    0..pos present); snap and run [H][d][d] are updated in place.  Returns
+    o [H][d]."""
+    torch = _torch()
+    T, H = _cpr_seq(q, k, v, alpha, beta)
+    if not 0 <= pos < T:
+        raise ValueError("pos must index a token of the sequence arrays")
+    d = q.shape[2]
+    if tuple(snap.shape) != (H, d, d) or tuple(run.shape) != (H, d, d):
+        raise ValueError("snap, run must be [H][d][d]")
+    if out is None:
+        out = torch.empty((H, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        ws, wsb = _workspace(cpr_workspace(c, H, c.leaf_size), q.device, None)
+    else:
+        ws, wsb = workspace, workspace.numel() * workspace.element_size()
+    _ok(lib.iso_cpr_decode_step(ctypes.byref(c), _bf16_ptr(q, "q"), _bf16_ptr(k, "k"),
+                                _bf16_ptr(v, "v"), _dev_ptr(alpha, "alpha", torch.float32),
+                                _dev_ptr(beta, "beta", torch.float32), pos,
+                                _dev_ptr(snap, "snap", torch.float32),
+                                _dev_ptr(run, "run", torch.float32),
+                                _dev_ptr(out, "out", torch.float32), H,
+                                None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
+        "iso_cpr_decode_step")
     return out
 
 

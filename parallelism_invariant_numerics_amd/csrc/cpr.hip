@@ -1,0 +1,350 @@
+// cpr.hip -- chunkwise-parallel recurrent (CPR) gated delta rule for gfx950.
+//
+// "IsoExec: Eliminating Trainer-Inference Mismatch in SkyRL" (agentlenshq),
+// section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet": the
+// recurrence is the numerical definition, evaluated in parallel across
+// chunks, and decode re-synchronises the hidden state every C tokens, so
+// trainer, prefill and decode give the same bits.  The pages give no GDN
+// equations; the gated delta rule used here is, per head with a d x d state S
+// (row a = value index, column j = key index):
+//     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t.
+//
+// One token step: u = S k, w = beta (v - alpha u), S <- alpha S + w k^T,
+// o = S q.  Every dot product is the balanced binary tree over the d = 128
+// products in index order (64 per lane, the two halves joined across a lane
+// pair), every other operation is one FP32 multiply or add in the order
+// written (no contraction), so the bits are those of a plain FP32
+// evaluation in the same order.
+//
+// CPR split, per head:
+//   chunk form   (P_c, U_c) of chunk c from its tokens alone, by the backward
+//                scan R = I, U = 0; for i = C-1 .. 0: r = k_i^T R,
+//                U <- U + (beta_i v_i) r, R <- alpha_i (R - (beta_i k_i) r);
+//                P_c = R.  All chunks in parallel.
+//   pass         B_{c+1} = U_c + B_c P_c (tree-ordered sums over the 128
+//                terms), sequential over chunks, parallel over state rows
+//                (a row of B_{c+1} needs only the same row of B_c).
+//   outputs      the token steps of chunk c started from B_c, all chunks in
+//                parallel.
+//   decode       the same token step on the running state; a token that
+//                closes a chunk replaces the running state by B_{c+1} from
+//                the chunk form (the re-sync), exactly as prefill does.
+//
+// Layouts: q, k, v [T][H][128] bf16; alpha, beta [T][H] FP32; states
+// [H][128][128] FP32 row-major; P, U, boundary states [chunk][H][128][128].
+#include "device_common.hpp"
+#include "kernels.h"
+
+namespace iso {
+
+constexpr int kCprD = 128;
+constexpr int kCprThreads = 256;
+constexpr int kCprMaxChunk = 64;
+constexpr int kCprPassRows = 8;  // state rows per workgroup of the pass
+
+// Balanced tree over p[0..64) in index order (pairs (2i, 2i+1) per level).
+__device__ __forceinline__ float tree64(float (&p)[64])
+{
+#pragma unroll
+    for (int w = 64; w > 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i)
+            p[i] = p[2 * i] + p[2 * i + 1];
+    return p[0];
+}
+
+// The top tree level: this lane's half plus its partner's (lane ^ 1); both
+// lanes get the same bits (IEEE addition is commutative).
+__device__ __forceinline__ float pair_join(float x) { return x + dpp_mov<0xB1>(x); }
+
+// 64 bf16 values (8 x 16 bytes) from LDS, widened.
+__device__ __forceinline__ void lds_bf16x64(const uint16_t *src, float (&dst)[64])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const u32x4 w = reinterpret_cast<const u32x4 *>(src)[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            dst[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+            dst[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+}
+
+// One token step on this lane's half row S (columns 64 hf .. 64 hf + 63 of
+// row a).  k_row, q_row: the token's k and q rows in LDS; returns o[a].
+__device__ __forceinline__ float cpr_token_step(float (&S)[64], const uint16_t *k_row,
+                                                const uint16_t *q_row, float v_a, float alpha,
+                                                float beta, int hf)
+{
+    float kk[64], p[64];
+    lds_bf16x64(k_row + 64 * hf, kk);
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        p[j] = S[j] * kk[j];
+    const float u = pair_join(tree64(p));
+    const float w = beta * (v_a - alpha * u);
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        S[j] = alpha * S[j] + w * kk[j];
+    float qq[64];
+    lds_bf16x64(q_row + 64 * hf, qq);
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+        p[j] = S[j] * qq[j];
+    return pair_join(tree64(p));
+}
+
+// Stage n token rows (128 bf16 each) of head h from [T][H][128] into
+// dst[n][128], 16 bytes per thread and step.
+__device__ __forceinline__ void stage_rows(const uint16_t *src, int64_t t0, int n, int64_t H,
+                                           int64_t h, uint16_t (*dst)[kCprD])
+{
+    for (int e = threadIdx.x; e < n * 16; e += kCprThreads) {
+        const int tok = e >> 4, part = e & 15;
+        const u32x4 w =
+            *reinterpret_cast<const u32x4 *>(src + ((t0 + tok) * H + h) * kCprD + part * 8);
+        *reinterpret_cast<u32x4 *>(&dst[tok][part * 8]) = w;
+    }
+}
+
+// Outputs of chunk blockIdx.y of head blockIdx.x: token steps from its
+// boundary state bounds[c] ([c][H][128][128]).  The last chunk may be partial
+// (T not a multiple of C): its stepped state goes to run_out.
+__global__ __launch_bounds__(kCprThreads) void cpr_output_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta,
+    const float *__restrict__ bounds, float *__restrict__ o, float *__restrict__ run_out, int64_t T,
+    int64_t H, int C)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kCprMaxChunk][kCprD];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[kCprMaxChunk][kCprD];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kCprMaxChunk][kCprD];
+    __shared__ float al[kCprMaxChunk], be[kCprMaxChunk];
+    const int64_t h = blockIdx.x;
+    const int64_t c = blockIdx.y;
+    const int64_t t0 = c * C;
+    const int n = static_cast<int>(T - t0 < C ? T - t0 : C);
+    stage_rows(k, t0, n, H, h, ks);
+    stage_rows(q, t0, n, H, h, qs);
+    stage_rows(v, t0, n, H, h, vs);
+    for (int e = threadIdx.x; e < n; e += kCprThreads) {
+        al[e] = alpha[(t0 + e) * H + h];
+        be[e] = beta[(t0 + e) * H + h];
+    }
+    __syncthreads();
+    const int a = threadIdx.x >> 1, hf = threadIdx.x & 1;
+    float S[64];
+    const float *B = bounds + ((c * H + h) * kCprD + a) * kCprD + 64 * hf;
+#pragma unroll
+    for (int j = 0; j < 64; j += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(B + j);
+        S[j] = x[0];
+        S[j + 1] = x[1];
+        S[j + 2] = x[2];
+        S[j + 3] = x[3];
+    }
+    for (int i = 0; i < n; ++i) {
+        const float va = bf16_to_f32(vs[i][a]);
+        const float oa = cpr_token_step(S, ks[i], qs[i], va, al[i], be[i], hf);
+        if (hf == 0)
+            o[((t0 + i) * H + h) * kCprD + a] = oa;
+    }
+    if (n < C && run_out) {
+        float *R = run_out + (h * kCprD + a) * kCprD + 64 * hf;
+#pragma unroll
+        for (int j = 0; j < 64; j += 4)
+            *reinterpret_cast<f32x4 *>(R + j) = f32x4{S[j], S[j + 1], S[j + 2], S[j + 3]};
+    }
+}
+
+// Chunk form (P, U) of chunk blockIdx.y of head blockIdx.x, its tokens
+// starting at t_first + blockIdx.y * C.  Lane pair j holds column j of R and
+// of U, rows 64 hf .. 64 hf + 63 each.
+__global__ __launch_bounds__(kCprThreads) void cpr_transition_kernel(
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta, float *__restrict__ P,
+    float *__restrict__ U, int64_t t_first, int64_t H, int C)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kCprMaxChunk][kCprD];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kCprMaxChunk][kCprD];
+    __shared__ float al[kCprMaxChunk], be[kCprMaxChunk];
+    const int64_t h = blockIdx.x;
+    const int64_t c = blockIdx.y;
+    const int64_t t0 = t_first + c * C;
+    stage_rows(k, t0, C, H, h, ks);
+    stage_rows(v, t0, C, H, h, vs);
+    for (int e = threadIdx.x; e < C; e += kCprThreads) {
+        al[e] = alpha[(t0 + e) * H + h];
+        be[e] = beta[(t0 + e) * H + h];
+    }
+    __syncthreads();
+    const int j = threadIdx.x >> 1, hf = threadIdx.x & 1;
+    float R[64], Uc[64];
+#pragma unroll
+    for (int mi = 0; mi < 64; ++mi) {
+        R[mi] = (64 * hf + mi == j) ? 1.0f : 0.0f;
+        Uc[mi] = 0.0f;
+    }
+    for (int i = C - 1; i >= 0; --i) {
+        float kk[64], p[64];
+        lds_bf16x64(ks[i] + 64 * hf, kk);
+#pragma unroll
+        for (int mi = 0; mi < 64; ++mi)
+            p[mi] = kk[mi] * R[mi];
+        const float r = pair_join(tree64(p));
+        const float a_i = al[i], b_i = be[i];
+        float vv[64];
+        lds_bf16x64(vs[i] + 64 * hf, vv);
+#pragma unroll
+        for (int ai = 0; ai < 64; ++ai) {
+            const float t = b_i * vv[ai];
+            Uc[ai] = Uc[ai] + t * r;
+        }
+#pragma unroll
+        for (int mi = 0; mi < 64; ++mi) {
+            const float s = b_i * kk[mi];
+            R[mi] = a_i * (R[mi] - s * r);
+        }
+    }
+    float *Pc = P + (c * H + h) * kCprD * kCprD + j;
+    float *Ucp = U + (c * H + h) * kCprD * kCprD + j;
+#pragma unroll
+    for (int mi = 0; mi < 64; ++mi) {
+        Pc[(64 * hf + mi) * kCprD] = R[mi];
+        Ucp[(64 * hf + mi) * kCprD] = Uc[mi];
+    }
+}
+
+// Boundary pass for head blockIdx.x, state rows 8 blockIdx.y .. +7:
+// B_{c+1} = U_c + B_c P_c for c < nb, from B_0 = S0 (zeros when null).
+// bounds (optional) receives B_0 .. B_nb; snap receives B_nb, and run too
+// when given.  S0 may alias snap (rows are read before they are written,
+// each by the workgroup that owns them).
+__global__ __launch_bounds__(kCprThreads) void cpr_pass_kernel(
+    const float *__restrict__ P, const float *__restrict__ U, const float *S0, float *bounds,
+    float *snap, float *run, int64_t H, int64_t nb)
+{
+    __shared__ __attribute__((aligned(16))) float B[kCprPassRows][kCprD];
+    const int64_t h = blockIdx.x;
+    const int r = threadIdx.x >> 5;
+    const int j0 = (threadIdx.x & 31) * 4;
+    const int64_t a = static_cast<int64_t>(blockIdx.y) * kCprPassRows + r;
+    const int64_t row = (h * kCprD + a) * kCprD + j0;  // offset of (h, a, j0) in a state
+    const int64_t state = H * kCprD * kCprD;            // one [H][128][128] block
+    f32x4 b0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (S0)
+        b0 = *reinterpret_cast<const f32x4 *>(S0 + row);
+    *reinterpret_cast<f32x4 *>(&B[r][j0]) = b0;
+    if (bounds)
+        *reinterpret_cast<f32x4 *>(bounds + row) = b0;
+    __syncthreads();
+    for (int64_t c = 0; c < nb; ++c) {
+        const float *Pc = P + c * state + h * kCprD * kCprD + j0;
+        float st[4][7];
+        float root[4];
+#pragma unroll
+        for (int m = 0; m < kCprD; ++m) {
+            const float bm = B[r][m];
+            const f32x4 pm = *reinterpret_cast<const f32x4 *>(Pc + m * kCprD);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // binary counter over the 128 products: the trailing ones of
+                // m are the saved left siblings this product closes
+                const int ones = __builtin_ctz(~static_cast<unsigned>(m));
+                float x = bm * pm[e];
+                for (int lvl = 0; lvl < ones; ++lvl)
+                    x = st[e][lvl] + x;
+                if (ones < 7)
+                    st[e][ones] = x;
+                else
+                    root[e] = x;
+            }
+        }
+        const f32x4 u = *reinterpret_cast<const f32x4 *>(U + c * state + row);
+        const f32x4 nxt = f32x4{u[0] + root[0], u[1] + root[1], u[2] + root[2], u[3] + root[3]};
+        __syncthreads();  // every lane has read B_c
+        *reinterpret_cast<f32x4 *>(&B[r][j0]) = nxt;
+        if (bounds)
+            *reinterpret_cast<f32x4 *>(bounds + (c + 1) * state + row) = nxt;
+        __syncthreads();
+    }
+    const f32x4 fin = *reinterpret_cast<const f32x4 *>(&B[r][j0]);
+    *reinterpret_cast<f32x4 *>(snap + row) = fin;
+    if (run)
+        *reinterpret_cast<f32x4 *>(run + row) = fin;
+}
+
+// One decode step of token `pos` for every head: the running state run
+// [H][128][128] is stepped in place and o [H][128] written.
+__global__ __launch_bounds__(kCprThreads) void cpr_decode_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ beta, int64_t pos,
+    float *__restrict__ run, float *__restrict__ o, int64_t H)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t ks[1][kCprD];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[1][kCprD];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[1][kCprD];
+    const int64_t h = blockIdx.x;
+    stage_rows(k, pos, 1, H, h, ks);
+    stage_rows(q, pos, 1, H, h, qs);
+    stage_rows(v, pos, 1, H, h, vs);
+    __syncthreads();
+    const int a = threadIdx.x >> 1, hf = threadIdx.x & 1;
+    float *Srow = run + (h * kCprD + a) * kCprD + 64 * hf;
+    float S[64];
+#pragma unroll
+    for (int j = 0; j < 64; j += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(Srow + j);
+        S[j] = x[0];
+        S[j + 1] = x[1];
+        S[j + 2] = x[2];
+        S[j + 3] = x[3];
+    }
+    const float oa = cpr_token_step(S, ks[0], qs[0], bf16_to_f32(vs[0][a]), alpha[pos * H + h],
+                                    beta[pos * H + h], hf);
+    if (hf == 0)
+        o[h * kCprD + a] = oa;
+#pragma unroll
+    for (int j = 0; j < 64; j += 4)
+        *reinterpret_cast<f32x4 *>(Srow + j) = f32x4{S[j], S[j + 1], S[j + 2], S[j + 3]};
+}
+
+hipError_t launch_cpr_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const float *alpha, const float *beta, const float *S0, float *o,
+                              float *snap, float *run, int64_t T, int64_t H, int C, float *P,
+                              float *U, float *bounds, hipStream_t stream)
+{
+    const int64_t nb = T / C;
+    const int64_t nchunks = (T + C - 1) / C;
+    if (nb > 0)
+        hipLaunchKernelGGL(cpr_transition_kernel, dim3(static_cast<unsigned>(H), static_cast<unsigned>(nb)),
+                           dim3(kCprThreads), 0, stream, k, v, alpha, beta, P, U, int64_t{0}, H, C);
+    hipLaunchKernelGGL(cpr_pass_kernel, dim3(static_cast<unsigned>(H), kCprD / kCprPassRows),
+                       dim3(kCprThreads), 0, stream, P, U, S0, bounds, snap,
+                       (T % C == 0) ? run : nullptr, H, nb);
+    if (nchunks > 0)
+        hipLaunchKernelGGL(cpr_output_kernel, dim3(static_cast<unsigned>(H), static_cast<unsigned>(nchunks)),
+                           dim3(kCprThreads), 0, stream, q, k, v, alpha, beta, bounds, o,
+                           (T % C == 0) ? nullptr : run, T, H, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_cpr_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *alpha, const float *beta, int64_t pos, float *snap,
+                             float *run, float *o, int64_t H, int C, float *P, float *U,
+                             hipStream_t stream)
+{
+    hipLaunchKernelGGL(cpr_decode_kernel, dim3(static_cast<unsigned>(H)), dim3(kCprThreads), 0, stream,
+                       q, k, v, alpha, beta, pos, run, o, H);
+    if ((pos + 1) % C == 0) {
+        hipLaunchKernelGGL(cpr_transition_kernel, dim3(static_cast<unsigned>(H), 1u), dim3(kCprThreads), 0,
+                           stream, k, v, alpha, beta, P, U, pos - (C - 1), H, C);
+        hipLaunchKernelGGL(cpr_pass_kernel, dim3(static_cast<unsigned>(H), kCprD / kCprPassRows),
+                           dim3(kCprThreads), 0, stream, P, U, snap, static_cast<float *>(nullptr),
+                           snap, run, H, int64_t{1});
+    }
+    return hipGetLastError();
+}
+
+}  // namespace iso

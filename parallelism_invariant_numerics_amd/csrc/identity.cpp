@@ -76,7 +76,7 @@ iso_status check_claims(const iso_composition &c)
         if (((c.claims >> b) & 1u) == 0)
             continue;
         const uint32_t p = 1u << b;
-        if (c.policy.schedule == ISO_SCHED_SEQ_KASC ? p != 1 : c.policy.leaf_count % p != 0)
+        if (c.policy.schedule != ISO_SCHED_MFMA16X16X32_KASC ? p != 1 : c.policy.leaf_count % p != 0)
             return ISO_ERR_CLAIM;
     }
     return ISO_OK;

@@ -139,6 +139,13 @@ iso_status iso_contract_validate(const iso_contract *c)
             return ISO_ERR_CONTRACT;
         return ISO_OK;
     }
+    if (c->schedule == ISO_SCHED_CPR_GDN) {
+        if (!is_pow2(c->leaf_count) || c->leaf_count > 4096)
+            return ISO_ERR_CONTRACT;
+        if (c->leaf_size < 1 || c->leaf_size > 64 || c->vocab_chunk != 0)
+            return ISO_ERR_CONTRACT;
+        return ISO_OK;
+    }
     return ISO_ERR_CONTRACT;
 }
 
@@ -439,6 +446,116 @@ iso_status iso_rmsnorm(const iso_contract *c, const void *x, const void *residua
         out_dtype == ISO_BF16 ? 1 : 0, M, H, (int)c->leaf_size, (int)(span / 8), eps,
         static_cast<hipStream_t>(stream)));
 }
+namespace {
+
+constexpr int64_t kCprHead = 128;
+
+struct CprLayout {
+    size_t P, U, bounds, total;
+};
+
+CprLayout cpr_layout(int64_t H, int64_t T, int64_t C)
+{
+    const size_t state = (size_t)H * kCprHead * kCprHead * sizeof(float);
+    const size_t nb = (size_t)(T / C);
+    CprLayout l;
+    l.P = 0;
+    l.U = align_up(nb * state);
+    l.bounds = l.U + align_up(nb * state);
+    l.total = l.bounds + align_up((nb + 1) * state);
+    return l;
+}
+
+iso_status cpr_check(const iso_contract *c, int64_t H, int64_t T)
+{
+    iso_status s = iso_contract_validate(c);
+    if (s != ISO_OK)
+        return s;
+    if (c->schedule != ISO_SCHED_CPR_GDN)
+        return ISO_ERR_CONTRACT;
+    if (c->leaf_count != kCprHead)
+        return ISO_ERR_SHAPE;
+    if (H < 1 || H >= 65536 || T < 0)
+        return ISO_ERR_ARG;
+    if ((T + c->leaf_size - 1) / c->leaf_size >= 65536)
+        return ISO_ERR_SHAPE;
+    return ISO_OK;
+}
+
+}  // namespace
+
+size_t iso_cpr_workspace(const iso_contract *c, int64_t H, int64_t T)
+{
+    if (cpr_check(c, H, T) != ISO_OK)
+        return (size_t)-1;
+    return cpr_layout(H, T, c->leaf_size).total;
+}
+
+iso_status iso_cpr_prefill(const iso_contract *c, const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, const float *S0, float *o,
+                           float *snap, float *run, int64_t T, int64_t H, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    iso_status s = cpr_check(c, H, T);
+    if (s != ISO_OK)
+        return s;
+    if (!snap || !run || snap == run || !aligned16(snap) || !aligned16(run))
+        return ISO_ERR_ARG;
+    if (S0 && !aligned16(S0))
+        return ISO_ERR_ARG;
+    if (T > 0) {
+        if (!q || !k || !v || !alpha || !beta || !o)
+            return ISO_ERR_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+            return ISO_ERR_ARG;
+        const void *ins[] = {q, k, v, alpha, beta, S0, snap, run};
+        for (const void *p : ins)
+            if (p == (const void *)o)
+                return ISO_ERR_ARG;
+    }
+    const CprLayout l = cpr_layout(H, T, c->leaf_size);
+    if (!workspace || workspace_bytes < l.total || !aligned16(workspace))
+        return ISO_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    clear_stale_error();
+    return launch_status(iso::launch_cpr_prefill(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), alpha, beta, S0, o, snap, run, T, H, (int)c->leaf_size,
+        reinterpret_cast<float *>(ws + l.P), reinterpret_cast<float *>(ws + l.U),
+        reinterpret_cast<float *>(ws + l.bounds), static_cast<hipStream_t>(stream)));
+}
+
+iso_status iso_cpr_decode_step(const iso_contract *c, const void *q, const void *k, const void *v,
+                               const float *alpha, const float *beta, int64_t pos, float *snap,
+                               float *run, float *o, int64_t H, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    iso_status s = cpr_check(c, H, c ? (int64_t)c->leaf_size : 0);
+    if (s != ISO_OK)
+        return s;
+    if (pos < 0 || pos >= ((int64_t)1 << 40))
+        return ISO_ERR_ARG;
+    if (!q || !k || !v || !alpha || !beta || !o || !snap || !run || snap == run)
+        return ISO_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(snap) ||
+        !aligned16(run))
+        return ISO_ERR_ARG;
+    const void *ins[] = {q, k, v, alpha, beta, snap, run};
+    for (const void *p : ins)
+        if (p == (const void *)o)
+            return ISO_ERR_ARG;
+    const CprLayout l = cpr_layout(H, c->leaf_size, c->leaf_size);
+    if (!workspace || workspace_bytes < l.total || !aligned16(workspace))
+        return ISO_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    clear_stale_error();
+    return launch_status(iso::launch_cpr_decode(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), alpha, beta, pos, snap, run, o, H, (int)c->leaf_size,
+        reinterpret_cast<float *>(ws + l.P), reinterpret_cast<float *>(ws + l.U),
+        static_cast<hipStream_t>(stream)));
+}
+
 iso_status iso_moe_layout_of(int64_t T, int64_t H, int64_t E, int64_t I, int top_k,
                              iso_moe_layout *out)
 {

@@ -46,6 +46,20 @@ hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *residual, uint16_t 
                           const uint16_t *weight, void *y, int out_bf16, int64_t M, int64_t H,
                           int leaf_size, int chunks, float eps, hipStream_t stream);
 
+// CPR gated delta rule, head size 128, chunk C (1..64).  Prefill: chunk
+// forms P, U [T/C][H][128][128], boundary states bounds [T/C + 1][H][128][128]
+// (workspace), outputs o, final snap / run.  Decode: one token step of every
+// head, plus the re-sync (chunk form into P, U [1][H][128][128], pass into
+// snap and run) when pos closes a chunk.
+hipError_t launch_cpr_prefill(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const float *alpha, const float *beta, const float *S0, float *o,
+                              float *snap, float *run, int64_t T, int64_t H, int C, float *P,
+                              float *U, float *bounds, hipStream_t stream);
+hipError_t launch_cpr_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *alpha, const float *beta, int64_t pos, float *snap,
+                             float *run, float *o, int64_t H, int C, float *P, float *U,
+                             hipStream_t stream);
+
 struct MoeBuffers {
     int32_t *idx;       // [T][k]
     float *gate;        // [T][k]
