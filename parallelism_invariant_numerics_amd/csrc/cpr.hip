@@ -220,11 +220,13 @@ __global__ __launch_bounds__(kCprThreads) void cpr_transition_kernel(
 // B_{c+1} = U_c + B_c P_c for c < nb, from B_0 = S0 (zeros when null).
 // bounds (optional) receives B_0 .. B_nb; snap receives B_nb, and run too
 // when given.  S0 may alias snap (rows are read before they are written,
-// each by the workgroup that owns them).
+// each by the workgroup that owns them).  P_c sits in LDS; the next chunk's
+// P and U are loaded into registers while this chunk is multiplied.
 __global__ __launch_bounds__(kCprThreads) void cpr_pass_kernel(
     const float *__restrict__ P, const float *__restrict__ U, const float *S0, float *bounds,
     float *snap, float *run, int64_t H, int64_t nb)
 {
+    __shared__ __attribute__((aligned(16))) float Ps[kCprD][kCprD];  // 64 KiB
     __shared__ __attribute__((aligned(16))) float B[kCprPassRows][kCprD];
     const int64_t h = blockIdx.x;
     const int r = threadIdx.x >> 5;
@@ -232,21 +234,42 @@ __global__ __launch_bounds__(kCprThreads) void cpr_pass_kernel(
     const int64_t a = static_cast<int64_t>(blockIdx.y) * kCprPassRows + r;
     const int64_t row = (h * kCprD + a) * kCprD + j0;  // offset of (h, a, j0) in a state
     const int64_t state = H * kCprD * kCprD;            // one [H][128][128] block
+    constexpr int kPer = kCprD * kCprD / 4 / kCprThreads;  // float4 of P per thread: 16
     f32x4 b0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (S0)
         b0 = *reinterpret_cast<const f32x4 *>(S0 + row);
     *reinterpret_cast<f32x4 *>(&B[r][j0]) = b0;
     if (bounds)
         *reinterpret_cast<f32x4 *>(bounds + row) = b0;
-    __syncthreads();
+    f32x4 pn[kPer];
+    f32x4 un = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (nb > 0) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(P + h * kCprD * kCprD);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+            pn[e] = src[e * kCprThreads + threadIdx.x];
+        un = *reinterpret_cast<const f32x4 *>(U + row);
+    }
     for (int64_t c = 0; c < nb; ++c) {
-        const float *Pc = P + c * state + h * kCprD * kCprD + j0;
+        // P_c into LDS (every lane has finished reading P_{c-1} and B_c is written)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e)
+            reinterpret_cast<f32x4 *>(&Ps[0][0])[e * kCprThreads + threadIdx.x] = pn[e];
+        const f32x4 u = un;
+        __syncthreads();
+        if (c + 1 < nb) {  // next chunk's P and U, in flight during the products
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(P + (c + 1) * state + h * kCprD * kCprD);
+#pragma unroll
+            for (int e = 0; e < kPer; ++e)
+                pn[e] = src[e * kCprThreads + threadIdx.x];
+            un = *reinterpret_cast<const f32x4 *>(U + (c + 1) * state + row);
+        }
         float st[4][7];
         float root[4];
 #pragma unroll
         for (int m = 0; m < kCprD; ++m) {
             const float bm = B[r][m];
-            const f32x4 pm = *reinterpret_cast<const f32x4 *>(Pc + m * kCprD);
+            const f32x4 pm = *reinterpret_cast<const f32x4 *>(&Ps[m][j0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // binary counter over the 128 products: the trailing ones of
@@ -261,14 +284,13 @@ __global__ __launch_bounds__(kCprThreads) void cpr_pass_kernel(
                     root[e] = x;
             }
         }
-        const f32x4 u = *reinterpret_cast<const f32x4 *>(U + c * state + row);
         const f32x4 nxt = f32x4{u[0] + root[0], u[1] + root[1], u[2] + root[2], u[3] + root[3]};
-        __syncthreads();  // every lane has read B_c
+        __syncthreads();  // every lane has read B_c and P_c
         *reinterpret_cast<f32x4 *>(&B[r][j0]) = nxt;
         if (bounds)
             *reinterpret_cast<f32x4 *>(bounds + (c + 1) * state + row) = nxt;
-        __syncthreads();
     }
+    __syncthreads();
     const f32x4 fin = *reinterpret_cast<const f32x4 *>(&B[r][j0]);
     *reinterpret_cast<f32x4 *>(snap + row) = fin;
     if (run)
