@@ -12,7 +12,9 @@ invariance-sweep shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8
 partitions, the LM-head logprob workload (8192 rows x 2048 x 151936
 vocabulary) in rows/s, the MoE FFN block (4096 tokens, 128 experts, top-8),
 the RMSNorm with residual add in front of the LM-head (8192 x 2048, GB/s),
-plus bitwise invariance checks.  Prints ONE JSON line.
+the CPR gated delta rule (16 heads of 128, 4096 tokens, chunk 64: prefill
+ms and decode us per token), plus bitwise invariance checks (CPR: decode of
+the last chunk equals the prefill).  Prints ONE JSON line.
 
 Inputs are seeded synthetic data with the workloads' shapes and
 distributions (no dataset or trained weights are involved).
@@ -33,6 +35,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# FP32 vector operations without FMA or packed pairs: 256 CUs x 4 SIMDs x 16
+# lanes x 2.4 GHz (the 157.3 TFLOP/s figure counts FMA and packed FP32 twice each)
+PEAK_FP32_OPS_T = 39.3
 
 
 def _args():
@@ -361,6 +366,50 @@ def main():
                             "gbs": round(n_bytes / (n_ms * 1e-3) / 1e9, 1),
                             "hbm_frac": round(n_bytes / (n_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del xn, rn, wn, yn, ron, y_ref
+
+        # ---------------- CPR gated delta rule: prefill and decode of one layer
+        from iso_synth import cpr_inputs
+        Tc, Hc, Dc, Cc = 4096, 16, 128, 64
+        xc = cpr_inputs(Tc, Hc, Dc, seed=601)
+        qc, kc, vc = _dev(xc["q"]), _dev(xc["k"]), _dev(xc["v"])
+        alc = torch.from_numpy(xc["alpha"]).to("cuda")
+        bec = torch.from_numpy(xc["beta"]).to("cuda")
+        cc = iso.cpr_contract(Cc)
+        wsc = torch.empty(iso.cpr_workspace(cc, Hc, Tc), dtype=torch.uint8, device="cuda")
+        oc = torch.empty((Tc, Hc, Dc), dtype=torch.float32, device="cuda")
+        snc = torch.empty((Hc, Dc, Dc), dtype=torch.float32, device="cuda")
+        rnc = torch.empty_like(snc)
+        run_c = lambda: iso.cpr_prefill(qc, kc, vc, alc, bec, cc, out=oc, snap=snc, run=rnc,
+                                        workspace=wsc)
+        run_c()
+        c_ms = _time_events(run_c, max(5, args.steps // 5), stream)
+        # decode of the last chunk (64 steps, the last one re-syncs) from a prefill of the rest
+        T0 = Tc - Cc
+        _, sd, rd = iso.cpr_prefill(qc[:T0], kc[:T0], vc[:T0], alc[:T0], bec[:T0], cc)
+        wsd = torch.empty(iso.cpr_workspace(cc, Hc, Cc), dtype=torch.uint8, device="cuda")
+        od = torch.empty((Cc, Hc, Dc), dtype=torch.float32, device="cuda")
+        for p_ in range(T0, Tc):
+            iso.cpr_decode_step(qc, kc, vc, alc, bec, p_, sd, rd, cc, out=od[p_ - T0], workspace=wsd)
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(od.view(torch.int32), oc[T0:].view(torch.int32)))
+        ok &= bool(torch.equal(sd.view(torch.int32), snc.view(torch.int32)))
+        ok &= bool(torch.equal(rd.view(torch.int32), rnc.view(torch.int32)))
+
+        def dec_chunk():
+            for p_ in range(T0, Tc):
+                iso.cpr_decode_step(qc, kc, vc, alc, bec, p_, sd, rd, cc, out=od[p_ - T0],
+                                    workspace=wsd)
+        d_ms = _time_events(dec_chunk, 3, stream) / Cc
+        # FP32 operations per token and head: step ~7 d^2, chunk form ~7 d^2,
+        # boundary pass 2 d^3 / C (d = 128, C = 64)
+        c_ops = Tc * Hc * (14.0 * Dc * Dc + 2.0 * Dc ** 3 / Cc)
+        extra["cpr"] = {"shape": "16 heads of 128, 4096 tokens, chunk 64 (CPR gated delta rule)",
+                        "prefill_ms": round(c_ms, 4),
+                        "prefill_tokens_per_s": round(Tc / (c_ms * 1e-3), 1),
+                        "decode_us_per_token": round(d_ms * 1e3, 2),
+                        "alu_tops": round(c_ops / (c_ms * 1e-3) / 1e12, 2),
+                        "alu_frac": round(c_ops / (c_ms * 1e-3) / 1e12 / PEAK_FP32_OPS_T, 4)}
+        del qc, kc, vc, alc, bec, wsc, oc, snc, rnc, sd, rd, wsd, od
 
     extra["bitwise_pass"] = ok
     line["bitwise_pass"] = ok

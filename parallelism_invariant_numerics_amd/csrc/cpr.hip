@@ -42,33 +42,42 @@ constexpr int kCprThreads = 256;
 constexpr int kCprMaxChunk = 64;
 constexpr int kCprPassRows = 8;  // state rows per workgroup of the pass
 
-// Balanced tree over p[0..64) in index order (pairs (2i, 2i+1) per level).
-__device__ __forceinline__ float tree64(float (&p)[64])
-{
-#pragma unroll
-    for (int w = 64; w > 1; w >>= 1)
-#pragma unroll
-        for (int i = 0; i < w / 2; ++i)
-            p[i] = p[2 * i] + p[2 * i + 1];
-    return p[0];
-}
-
 // The top tree level: this lane's half plus its partner's (lane ^ 1); both
 // lanes get the same bits (IEEE addition is commutative).
 __device__ __forceinline__ float pair_join(float x) { return x + dpp_mov<0xB1>(x); }
 
-// 64 bf16 values (8 x 16 bytes) from LDS, widened.
-__device__ __forceinline__ void lds_bf16x64(const uint16_t *src, float (&dst)[64])
+// bf16 element e (0..7) of a 16-byte LDS chunk, widened.
+__device__ __forceinline__ float bf16_of(const u32x4 &w, int e)
 {
+    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+}
+
+// Balanced binary tree, in index order, over x[j] * y[j] for j < 64, with y a
+// bf16 row in LDS read 16 bytes at a time.  The tree is kept as a binary
+// counter: the trailing ones of j are the saved left siblings that product j
+// closes, so the additions and their operand order are those of the
+// level-by-level tree.
+__device__ __forceinline__ float dot64(const float (&x)[64], const uint16_t *y)
+{
+    float st[6];
+    float root = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        const u32x4 w = reinterpret_cast<const u32x4 *>(src)[c];
+        const u32x4 w = reinterpret_cast<const u32x4 *>(y)[c];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dst[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
-            dst[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        for (int e = 0; e < 8; ++e) {
+            const int j = 8 * c + e;
+            float t = x[j] * bf16_of(w, e);
+            const int ones = __builtin_ctz(~static_cast<unsigned>(j));
+            for (int l = 0; l < ones; ++l)
+                t = st[l] + t;
+            if (ones < 6)
+                st[ones] = t;
+            else
+                root = t;
         }
     }
+    return root;
 }
 
 // One token step on this lane's half row S (columns 64 hf .. 64 hf + 63 of
@@ -77,22 +86,17 @@ __device__ __forceinline__ float cpr_token_step(float (&S)[64], const uint16_t *
                                                 const uint16_t *q_row, float v_a, float alpha,
                                                 float beta, int hf)
 {
-    float kk[64], p[64];
-    lds_bf16x64(k_row + 64 * hf, kk);
-#pragma unroll
-    for (int j = 0; j < 64; ++j)
-        p[j] = S[j] * kk[j];
-    const float u = pair_join(tree64(p));
+    const uint16_t *kh = k_row + 64 * hf;
+    const float u = pair_join(dot64(S, kh));
     const float w = beta * (v_a - alpha * u);
 #pragma unroll
-    for (int j = 0; j < 64; ++j)
-        S[j] = alpha * S[j] + w * kk[j];
-    float qq[64];
-    lds_bf16x64(q_row + 64 * hf, qq);
+    for (int c = 0; c < 8; ++c) {
+        const u32x4 kw = reinterpret_cast<const u32x4 *>(kh)[c];
 #pragma unroll
-    for (int j = 0; j < 64; ++j)
-        p[j] = S[j] * qq[j];
-    return pair_join(tree64(p));
+        for (int e = 0; e < 8; ++e)
+            S[8 * c + e] = alpha * S[8 * c + e] + w * bf16_of(kw, e);
+    }
+    return pair_join(dot64(S, q_row + 64 * hf));
 }
 
 // Stage n token rows (128 bf16 each) of head h from [T][H][128] into
@@ -187,24 +191,21 @@ __global__ __launch_bounds__(kCprThreads) void cpr_transition_kernel(
         Uc[mi] = 0.0f;
     }
     for (int i = C - 1; i >= 0; --i) {
-        float kk[64], p[64];
-        lds_bf16x64(ks[i] + 64 * hf, kk);
-#pragma unroll
-        for (int mi = 0; mi < 64; ++mi)
-            p[mi] = kk[mi] * R[mi];
-        const float r = pair_join(tree64(p));
+        const uint16_t *kh = ks[i] + 64 * hf;
+        const uint16_t *vh = vs[i] + 64 * hf;
+        const float r = pair_join(dot64(R, kh));  // products R[m] k[m] = k[m] R[m]
         const float a_i = al[i], b_i = be[i];
-        float vv[64];
-        lds_bf16x64(vs[i] + 64 * hf, vv);
 #pragma unroll
-        for (int ai = 0; ai < 64; ++ai) {
-            const float t = b_i * vv[ai];
-            Uc[ai] = Uc[ai] + t * r;
-        }
+        for (int cc = 0; cc < 8; ++cc) {
+            const u32x4 vw = reinterpret_cast<const u32x4 *>(vh)[cc];
+            const u32x4 kw = reinterpret_cast<const u32x4 *>(kh)[cc];
 #pragma unroll
-        for (int mi = 0; mi < 64; ++mi) {
-            const float s = b_i * kk[mi];
-            R[mi] = a_i * (R[mi] - s * r);
+            for (int e = 0; e < 8; ++e) {
+                const float t = b_i * bf16_of(vw, e);
+                Uc[8 * cc + e] = Uc[8 * cc + e] + t * r;
+                const float sm = b_i * bf16_of(kw, e);
+                R[8 * cc + e] = a_i * (R[8 * cc + e] - sm * r);
+            }
         }
     }
     float *Pc = P + (c * H + h) * kCprD * kCprD + j;
