@@ -49,6 +49,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict
     const int64_t c0 = static_cast<int64_t>(lane) * S;
     const bool active = c0 < H;
 
+    // the weight chunk, requested with the row so that its latency overlaps
+    // the row's loads instead of following the reduction
+    u32x4 wv[NCH];
+    if (active) {
+        const u32x4 *wp = reinterpret_cast<const u32x4 *>(w + c0);
+#pragma unroll
+        for (int k = 0; k < NCH; ++k)
+            wv[k] = wp[k];
+    }
+
     // h = x or bf16(x + residual), two bf16 per word
     uint32_t h[4 * NCH];
     if (active) {
@@ -114,30 +124,27 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict
 
     if (!active)
         return;
-    const u32x4 *wp = reinterpret_cast<const u32x4 *>(w + c0);
     if (out_bf16) {
         u32x4 *op = reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + row * H + c0);
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const u32x4 wv = wp[k];
             u32x4 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                o[q] = pack_bf16((bf16_lo(h[4 * k + q]) * rs) * bf16_lo(wv[q]),
-                                 (bf16_hi(h[4 * k + q]) * rs) * bf16_hi(wv[q]));
+                o[q] = pack_bf16((bf16_lo(h[4 * k + q]) * rs) * bf16_lo(wv[k][q]),
+                                 (bf16_hi(h[4 * k + q]) * rs) * bf16_hi(wv[k][q]));
             op[k] = o;
         }
     } else {
         f32x4 *op = reinterpret_cast<f32x4 *>(static_cast<float *>(y) + row * H + c0);
 #pragma unroll
         for (int k = 0; k < NCH; ++k) {
-            const u32x4 wv = wp[k];
 #pragma unroll
             for (int q = 0; q < 4; q += 2)
-                op[2 * k + q / 2] = f32x4{(bf16_lo(h[4 * k + q]) * rs) * bf16_lo(wv[q]),
-                                          (bf16_hi(h[4 * k + q]) * rs) * bf16_hi(wv[q]),
-                                          (bf16_lo(h[4 * k + q + 1]) * rs) * bf16_lo(wv[q + 1]),
-                                          (bf16_hi(h[4 * k + q + 1]) * rs) * bf16_hi(wv[q + 1])};
+                op[2 * k + q / 2] = f32x4{(bf16_lo(h[4 * k + q]) * rs) * bf16_lo(wv[k][q]),
+                                          (bf16_hi(h[4 * k + q]) * rs) * bf16_hi(wv[k][q]),
+                                          (bf16_lo(h[4 * k + q + 1]) * rs) * bf16_lo(wv[k][q + 1]),
+                                          (bf16_hi(h[4 * k + q + 1]) * rs) * bf16_hi(wv[k][q + 1])};
         }
     }
 }
