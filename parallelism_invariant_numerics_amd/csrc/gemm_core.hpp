@@ -244,19 +244,11 @@ __device__ __forceinline__ void stage_dma(const Pipe &p, char *lds, int st, int 
 
 // Wait until at most `pending` later stages of this wave's buffer loads
 // (2 kDma loads per stage) are still in flight, then synchronise the
-// workgroup.  The count is exact only while nothing but loads is in flight:
-// loads complete in order, but a store (a register spill) may complete before
-// an older load and make "at most n outstanding" true too early.  Kernel
-// instantiations whose register allocation spills set DRAIN, which waits for
-// every outstanding operation instead.
-template <class C, bool DRAIN = false>
+// workgroup.
+template <class C>
 __device__ __forceinline__ void stage_barrier(int pending)
 {
     constexpr int D = 2 * C::kDma;
-    if constexpr (DRAIN) {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        return;
-    }
     if (pending >= 2)
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * D) : "memory");
     else if (pending == 1)
@@ -322,7 +314,7 @@ __device__ __forceinline__ void pipe_prologue(const Pipe &p, char *lds, int nst)
 // the barrier: while one wave of a SIMD waits on the address unit, the other
 // one keeps the matrix core busy.  The loads still go out before the next
 // stage's wait, so the ring's counts are unchanged.
-template <class C, int LOG, bool PROLOGUE = true, bool DRAIN = false>
+template <class C, int LOG, bool PROLOGUE = true>
 __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char *lds,
                                                    Acc<C> &root)
 {
@@ -361,7 +353,7 @@ __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char 
         for (int s = 0; s < spl; ++s, ++st) {
             frag_wait(f1);  // previous stage's reads done before its buffer is recycled
             const int ahead = nst - 1 - st;
-            stage_barrier<C, DRAIN>(ahead < NB - 2 ? ahead : NB - 2);
+            stage_barrier<C>(ahead < NB - 2 ? ahead : NB - 2);
             const bool dma = st + NB - 1 < nst;
             if (dma && !late)
                 stage_dma<C>(p, lds, st + NB - 1, (st + NB - 1) % NB);

@@ -230,9 +230,7 @@ __global__ __launch_bounds__(C::kThreads, 2) void lmhead_fused_kernel(LmArgs a)
         Acc<C> z;
         {
             const Pipe pipe = lm_tile<C>(a, w, tm, tn, m0, n0);
-            // 16 leaves per workgroup spill a register after the first
-            // prologue: wait for everything at each stage (stage_barrier)
-            leaf_tree_mainloop<C, LOG, false, (LOG >= 4)>(pipe, a.stages_per_leaf, lds, z);
+            leaf_tree_mainloop<C, LOG, false>(pipe, a.stages_per_leaf, lds, z);
         }
         const int wn = w + slots;
         if (wn < end) {
@@ -348,9 +346,7 @@ __global__ __launch_bounds__(256) void lmhead_finish_kernel(const float *stats,
 template <int LOG>
 static hipError_t launch_fused(const LmArgs &a, hipStream_t stream)
 {
-    // the eight-wave shape at every depth: the two-workgroup shape spills
-    // inside its tile loop here (see stage_barrier)
-    using C = CfgWide;
+    using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
     const int64_t tiles = ((a.M + BM - 1) / BM) * a.nchunk;
     const int64_t slots = static_cast<int64_t>(device_cus()) * (C::kWaves == 4 ? 2 : 1);
     int64_t g = tiles < slots ? tiles : slots;

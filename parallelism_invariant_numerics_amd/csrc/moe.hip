@@ -487,12 +487,6 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs &a, const MoeTask
 // stages are requested right after it, before the epilogue, which stages
 // through its own LDS.  Otherwise (four-wave shape, two workgroups per CU)
 // each task runs start to end and the epilogue stages through the ring.
-// Depths whose register allocation spills inside the task loop (the
-// two-workgroup shape at 2 leaves, the eight-wave shape at 8 and 16 leaves)
-// wait for every outstanding operation at each ring stage (stage_barrier).
-template <class C, int LOG>
-constexpr bool kMoeDrain = (C::kWaves == 4 && LOG >= 1) || LOG >= 3;
-
 template <class C, int LOG, bool GATE_UP>
 __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(
     MoeGemmArgs a, const int32_t *__restrict__ tiles, const int32_t *__restrict__ counts,
@@ -533,12 +527,12 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(
             const Pipe p = moe_pipe<C, GATE_UP>(a, t, rows_s[b]);
             if (wn < end)
                 rows_dma(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]);
-            leaf_tree_mainloop<C, LOG, false, kMoeDrain<C, LOG>>(p, a.stages_per_leaf, lds, r0);
+            leaf_tree_mainloop<C, LOG, false>(p, a.stages_per_leaf, lds, r0);
             if (wn < end)
                 pipe_prologue<C>(moe_pipe<C, GATE_UP>(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]),
                                  lds, nst);
         } else {
-            leaf_tree_mainloop<C, LOG, true, kMoeDrain<C, LOG>>(moe_pipe<C, GATE_UP>(a, t, rows_s[b]), a.stages_per_leaf,
+            leaf_tree_mainloop<C, LOG>(moe_pipe<C, GATE_UP>(a, t, rows_s[b]), a.stages_per_leaf,
                                        lds, r0);
             if (wn < end)
                 rows_dma(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]);
