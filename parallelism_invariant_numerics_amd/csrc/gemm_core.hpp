@@ -244,7 +244,11 @@ __device__ __forceinline__ void stage_dma(const Pipe &p, char *lds, int st, int 
 
 // Wait until at most `pending` later stages of this wave's buffer loads
 // (2 kDma loads per stage) are still in flight, then synchronise the
-// workgroup.
+// workgroup.  The count n is the number of loads this wave issued after the
+// awaited stage.  Loads complete in order, so while any load of that stage
+// is outstanding all n later loads are too: at least n + 1 operations are
+// in flight, whatever stores (epilogue writes, register spills) do, and the
+// wait cannot pass early.
 template <class C>
 __device__ __forceinline__ void stage_barrier(int pending)
 {
