@@ -198,7 +198,7 @@ def main():
                    "M": M, "N": N, "K": K, "leaves": L, "leaf_size": K // L, "partitions": 1},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(src_hash), "kernel": "gemm_persistent_kernel<CfgWide, 3>",
+                     "traffic": _traffic(src_hash), "kernel": "gemm_leaf_kernel<CfgWide, 3>",
                      "kernel_ms": round(kern_ms, 5), "algorithmic_flop": flop,
                      "source_hash": src_hash},
     }

@@ -74,124 +74,6 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_leaf_kernel(GemmParams p)
     }
 }
 
-// A tile's roots to the output through `stg` ([64][128] FP32, 32 KiB) in
-// two halves of 64 rows, with inline-assembly LDS access (loads of the next
-// tile into the ring may be in flight).  Ends with a workgroup barrier.
-template <class C>
-__device__ __forceinline__ void store_tile_halves(const Acc<C> &root, float *stg, void *out,
-                                                  int64_t ld, int64_t rows, int64_t cols,
-                                                  bool bf16_out)
-{
-    const int cmax = cols < BN ? static_cast<int>(cols) : BN;
-    // Opaque to the optimiser, so that the per-lane addresses below are
-    // recomputed per tile rather than hoisted out of the tile loop, where
-    // they would be held across the main loop.
-    int tid = static_cast<int>(threadIdx.x);
-    asm volatile("" : "+v"(tid));
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-        stage_half<C>(root, stg, h);
-        lds_barrier();
-        const int64_t rlim = rows - 64 * h;  // rows of this half inside the matrix
-        if (bf16_out) {
-            uint16_t *o = static_cast<uint16_t *>(out) + 64 * h * ld;
-            const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (ld % 8 == 0);
-            constexpr int UPT = 64 * 16 / C::kThreads;  // 8 columns per unit
-            f32x4 lo[UPT], hi[UPT];
-#pragma unroll
-            for (int k = 0; k < UPT; ++k) {
-                const int u = tid + k * C::kThreads;
-                const int row = u >> 4, q = u & 15;
-                lds_issue_b128(lo[k], staged_addr(stg, row, 2 * q));
-                lds_issue_b128(hi[k], staged_addr(stg, row, 2 * q + 1));
-            }
-            lds_wait();
-#pragma unroll
-            for (int k = 0; k < UPT; ++k) {
-                lds_pin(lo[k]);
-                lds_pin(hi[k]);
-                const int u = tid + k * C::kThreads;
-                const int row = u >> 4, q = u & 15;
-                if (row < rlim) {
-                    const float v[8] = {lo[k][0], lo[k][1], lo[k][2], lo[k][3],
-                                        hi[k][0], hi[k][1], hi[k][2], hi[k][3]};
-                    store8_bf16(o + row * ld + 8 * q, v, al && 8 * q + 8 <= cmax, cmax - 8 * q);
-                }
-            }
-        } else {
-            float *o = static_cast<float *>(out) + 64 * h * ld;
-            const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (ld % 4 == 0);
-            constexpr int UPT = 64 * 32 / C::kThreads;  // 4 columns per unit
-            f32x4 v[UPT];
-#pragma unroll
-            for (int k = 0; k < UPT; ++k) {
-                const int u = tid + k * C::kThreads;
-                lds_issue_b128(v[k], staged_addr(stg, u >> 5, u & 31));
-            }
-            lds_wait();
-#pragma unroll
-            for (int k = 0; k < UPT; ++k) {
-                lds_pin(v[k]);
-                const int u = tid + k * C::kThreads;
-                const int row = u >> 5, q = u & 31;
-                if (row < rlim)
-                    store4_f32(o + row * ld + 4 * q, v[k], al && 4 * q + 4 <= cmax, cmax - 4 * q);
-            }
-        }
-        lds_barrier();  // the half's LDS reads are done before the next half
-    }
-}
-
-// Persistent single-partition GEMM: the workgroups on XCD x take the
-// contiguous range [x per, (x+1) per) of the grouped tile order, stepping by
-// the number of workgroups per XCD.  After a tile's main loop the next
-// tile's first ring stages (buffers 0 .. NBUF-2) are requested, and the
-// epilogue stages the roots through the last buffer, so their latency
-// overlaps the stores.  Same arithmetic, same bits as gemm_leaf_kernel.
-template <class C, int LOG>
-__global__ __launch_bounds__(C::kThreads, 1) void gemm_persistent_kernel(GemmParams p)
-{
-    static_assert(C::NBUF >= 2 && kStageBytes >= 64 * 128 * 4, "the last buffer holds half a tile");
-    __shared__ __attribute__((aligned(16))) char lds[C::kLdsBytes];
-    float *stg = reinterpret_cast<float *>(lds + (C::NBUF - 1) * kStageBytes);
-    const int tm = static_cast<int>((p.M + BM - 1) / BM);
-    const int tn = static_cast<int>((p.N + BN - 1) / BN);
-    const int total = tm * tn;
-    const int xcd = blockIdx.x % kXcds;
-    const int slots = gridDim.x / kXcds;
-    const int per = (total + kXcds - 1) / kXcds;
-    const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
-    int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds;
-    if (w >= end)
-        return;
-    const int nst = (1 << LOG) * p.stages_per_leaf;
-    auto tile_pipe = [&](int t, int64_t &m0, int64_t &n0) {
-        int mt, nt;
-        grouped_tile(t, tm, tn, kTileGroup, mt, nt);
-        m0 = static_cast<int64_t>(mt) * BM;
-        n0 = static_cast<int64_t>(nt) * BN;
-        return make_pipe<C>(p.A + m0 * p.K, p.M - m0, p.Wt + n0 * p.K, p.N - n0, p.K, 0);
-    };
-    int64_t m0, n0;
-    pipe_prologue<C>(tile_pipe(w, m0, n0), lds, nst);
-    for (;;) {
-        Acc<C> root;
-        leaf_tree_mainloop<C, LOG, false>(tile_pipe(w, m0, n0), p.stages_per_leaf, lds, root);
-        const int wn = w + slots;
-        if (wn < end) {
-            int64_t m0n, n0n;
-            pipe_prologue<C>(tile_pipe(wn, m0n, n0n), lds, nst);
-        }
-        const bool bf16 = p.mode == kOutBF16;
-        void *o = bf16 ? static_cast<void *>(static_cast<uint16_t *>(p.out) + m0 * p.N + n0)
-                       : static_cast<void *>(static_cast<float *>(p.out) + m0 * p.N + n0);
-        store_tile_halves<C>(root, stg, o, p.N, p.M - m0, p.N - n0, bf16);
-        if (wn >= end)
-            break;
-        w = wn;
-    }
-}
-
 // Top log2(P) tree levels over the partition roots ws[p][M][N].
 template <int P>
 __global__ __launch_bounds__(256) void partition_combine_kernel(const float *ws, void *out,
@@ -219,15 +101,6 @@ static hipError_t launch_leaf(const GemmParams &p, int parts, hipStream_t stream
 {
     using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
     const int64_t tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
-    if (LOG >= 2 && LOG <= 3 && parts == 1 && p.mode != kOutWorkspace) {
-        // one resident workgroup per CU, a whole number of rounds over the XCDs
-        const int64_t slots = device_cus();
-        int64_t g = tiles < slots ? tiles : slots;
-        g = (g + kXcds - 1) / kXcds * kXcds;
-        hipLaunchKernelGGL((gemm_persistent_kernel<CfgWide, LOG>), dim3(static_cast<unsigned>(g)),
-                           dim3(CfgWide::kThreads), 0, stream, p);
-        return hipGetLastError();
-    }
     dim3 grid(static_cast<unsigned>(tiles * parts));
     hipLaunchKernelGGL((gemm_leaf_kernel<C, LOG>), grid, dim3(C::kThreads), 0, stream, p);
     return hipGetLastError();

@@ -353,6 +353,36 @@ __device__ __forceinline__ Pipe moe_pipe(const MoeGemmArgs &a, const MoeTask &t,
     return p;
 }
 
+// Rows 64h .. 64h+63 of a tile's roots (held by the waves of tile row h) into
+// `stg` [64][128] FP32, with the chunk swizzle of stage_tile.
+template <class C>
+__device__ __forceinline__ void stage_half(const Acc<C> &root, float *stg, int h)
+{
+    static_assert(C::WR == 2 && BM == 128, "two wave rows of 64 tile rows");
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave / C::WC, wc = wave % C::WC;
+    if (wr != h)
+        return;
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::JB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = tile_row<C>(lane, wr, i, r) - 64 * h;
+                const int col = tile_col<C>(lane, wc, j);
+                const int chunk = (col >> 2) ^ (((row >> 2) & 3) << 2);
+                lds_write_f32(lds_addr(stg + row * 128 + chunk * 4 + (col & 3)), root.v[i][j][r]);
+            }
+}
+
+// Columns 4c .. 4c+3 of row `row` of a [64][128] staging buffer (address).
+__device__ __forceinline__ uint32_t staged_addr(const float *stg, int row, int c)
+{
+    return lds_addr(stg + row * 128 + ((c ^ (((row >> 2) & 3) << 2)) << 2));
+}
+
 // Epilogue of one task: gate/up writes h = bf16(silu(G) U) (G in tile
 // columns 0..63, U in 64..127), down writes the FP32 roots; tile row r goes
 // to output row rows_s[r].  Two halves of 64 rows through `stg` (32 KiB).
