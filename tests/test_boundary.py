@@ -242,3 +242,81 @@ def test_lmhead_shard_rejections_before_launch():
     assert fin(FAKE, FAKE, FAKE, FAKE, 4, (1 << 20) + 1, None) == 2
     assert fin(None, FAKE, FAKE, FAKE, 4, 100, None) == 1
     assert fin(FAKE, FAKE, FAKE, FAKE, 0, 100, None) == 0
+
+
+F2, F3, F4, F5, F6 = (FAKE * i for i in (2, 3, 4, 5, 6))  # distinct aligned fake addresses
+
+
+def _cpr(c, T=64, H=2, q=FAKE, k=FAKE, v=FAKE, al=FAKE, be=FAKE, S0=None, o=F2, snap=F3, run=F4,
+         ws=F5, wsb=1 << 40):
+    return iso.lib.iso_cpr_prefill(ctypes.byref(c), q, k, v, al, be, S0, o, snap, run, T, H, ws,
+                                   wsb, None)
+
+
+def _cpr_dec(c, pos=20, H=2, o=F2, snap=F3, run=F4, ws=F5, wsb=1 << 40, q=FAKE):
+    return iso.lib.iso_cpr_decode_step(ctypes.byref(c), q, FAKE, FAKE, FAKE, FAKE, pos, snap, run,
+                                       o, H, ws, wsb, None)
+
+
+def test_cpr_workspace_is_three_state_regions():
+    """P_c and U_c for every closed chunk and the boundary states B_0..B_nb,
+    each H * d * d FP32 (a multiple of 256 bytes, so no padding)."""
+    c = iso.cpr_contract(16)
+    state = 2 * 128 * 128 * 4
+    for T in (0, 15, 16, 64, 70):
+        nb = T // 16
+        assert iso.cpr_workspace(c, 2, T) == (3 * nb + 1) * state
+    with pytest.raises(iso.IsoError):
+        iso.cpr_workspace(c, 0, 16)
+    with pytest.raises(iso.IsoError):
+        iso.cpr_workspace(iso.cpr_contract(16, head_size=64), 1, 16)
+
+
+def test_cpr_contract_rules():
+    with pytest.raises(iso.IsoError, match="ISO_ERR_CONTRACT"):
+        iso.cpr_contract(0)
+    with pytest.raises(iso.IsoError, match="ISO_ERR_CONTRACT"):
+        iso.cpr_contract(65)                     # chunk at most 64 tokens
+    with pytest.raises(iso.IsoError, match="ISO_ERR_CONTRACT"):
+        iso.contract(128, 16, 128, iso.SCHED_CPR)  # no vocabulary chunk
+    digests = {iso.digest(iso.cpr_contract(C)) for C in (1, 7, 64)}
+    assert len(digests) == 3
+
+
+def test_cpr_prefill_rejections_before_launch():
+    c = iso.cpr_contract(16)
+    assert _cpr(iso.contract(8, 256, 0)) == 8                 # not the CPR schedule
+    assert _cpr(iso.cpr_contract(16, head_size=64)) == 2      # head size 128 only
+    assert _cpr(c, H=0) == 1
+    assert _cpr(c, H=65536) == 1
+    assert _cpr(c, T=-1) == 1
+    assert _cpr(c, T=16 * 65536) == 2                         # 65536 chunks
+    assert _cpr(c, snap=None) == 1
+    assert _cpr(c, run=F3) == 1                               # snap and run alias
+    assert _cpr(c, snap=F3 + 4) == 1                          # 16-byte alignment
+    assert _cpr(c, S0=F6 + 8) == 1
+    assert _cpr(c, q=None) == 1
+    assert _cpr(c, k=FAKE + 2) == 1
+    assert _cpr(c, o=FAKE) == 1                               # o aliases an input
+    assert _cpr(c, o=F3) == 1                                 # o aliases snap
+    assert _cpr(c, S0=F6, o=F6) == 1                          # o aliases S0
+    need = iso.cpr_workspace(c, 2, 64)
+    assert _cpr(c, ws=None) == 6
+    assert _cpr(c, wsb=need - 1) == 6
+    assert _cpr(c, ws=F5 + 8) == 6
+
+
+def test_cpr_decode_rejections_before_launch():
+    c = iso.cpr_contract(16)
+    assert _cpr_dec(iso.contract(8, 256, 0)) == 8
+    assert _cpr_dec(c, H=0) == 1
+    assert _cpr_dec(c, pos=-1) == 1
+    assert _cpr_dec(c, pos=1 << 40) == 1
+    assert _cpr_dec(c, run=F3) == 1
+    assert _cpr_dec(c, o=F4) == 1
+    assert _cpr_dec(c, o=FAKE) == 1
+    assert _cpr_dec(c, q=None) == 1
+    assert _cpr_dec(c, snap=F3 + 4) == 1
+    need = iso.cpr_workspace(c, 2, 16)
+    assert _cpr_dec(c, wsb=need - 1) == 6
+    assert _cpr_dec(c, ws=None) == 6
