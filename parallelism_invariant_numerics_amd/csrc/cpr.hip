@@ -218,84 +218,174 @@ __global__ __launch_bounds__(kCprThreads) void cpr_transition_kernel(
 }
 
 // Boundary pass for head blockIdx.x, state rows 8 blockIdx.y .. +7:
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
+}
+
+template <class T>
+__device__ __forceinline__ void lds_pin(T &v)
+{
+    asm volatile("" : "+v"(v));
+}
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait()
+{
+    static_assert(N >= 0 && N <= 15, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+
+constexpr int kBlk = 8;                // terms per pipelined block of the pass
+constexpr int kCprPassThreads = 512;   // two waves per SIMD
+
+// LDS reads of terms M and M + 1 of the pass for a lane's 1 x 2 outputs:
+// B[row][m], B[row][m+1] (8 bytes, the same address for every lane of a
+// wave) and P[m][2q .. 2q+1], P[m+1][2q .. 2q+1] (rows 512 bytes apart: one
+// ds_read2st64_b64 with offsets in units of 512 bytes).  Offsets are
+// immediates: the largest, 127 x 512 bytes and 126 x 4 bytes, fit the
+// instruction fields.
+template <int M>
+__device__ __forceinline__ void pass_pair_issue(f32x2 &b, f32x4 &p, uint32_t pa, uint32_t ba)
+{
+    asm volatile("ds_read2st64_b64 %0, %1 offset0:%2 offset1:%3"
+                 : "=v"(p)
+                 : "v"(pa), "n"(M), "n"(M + 1));
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(b) : "v"(ba), "n"(4 * M));
+}
+
+template <int K>
+__device__ __forceinline__ void pass_block_issue(f32x2 (&bq)[kBlk / 2], f32x4 (&pq)[kBlk / 2],
+                                                 uint32_t pa, uint32_t ba)
+{
+    static_assert(kBlk == 8, "four pairs of terms");
+    pass_pair_issue<K * kBlk + 0>(bq[0], pq[0], pa, ba);
+    pass_pair_issue<K * kBlk + 2>(bq[1], pq[1], pa, ba);
+    pass_pair_issue<K * kBlk + 4>(bq[2], pq[2], pa, ba);
+    pass_pair_issue<K * kBlk + 6>(bq[3], pq[3], pa, ba);
+}
+
 // B_{c+1} = U_c + B_c P_c for c < nb, from B_0 = S0 (zeros when null).
 // bounds (optional) receives B_0 .. B_nb; snap receives B_nb, and run too
 // when given.  S0 may alias snap (rows are read before they are written,
-// each by the workgroup that owns them).  P_c sits in LDS; the next chunk's
-// P and U are loaded into registers while this chunk is multiplied.
-__global__ __launch_bounds__(kCprThreads) void cpr_pass_kernel(
+// each by the workgroup that owns them).
+//
+// A workgroup of eight waves owns 8 rows of one head; wave s computes row s
+// and lane q columns 2q, 2q + 1: two products per term m from one value of
+// B_c (a broadcast read) and two of P_c (consecutive across the lanes).  Two
+// waves per SIMD hide each other's LDS and dependency latency.  P and B are
+// double-buffered in LDS, so one barrier per chunk separates the reads of
+// chunk c from the writes for chunk c + 1; P_{c+1} is written to LDS and
+// P_{c+2} and U_{c+1} are loaded into registers while chunk c is multiplied.
+__global__ __launch_bounds__(kCprPassThreads) void cpr_pass_kernel(
     const float *__restrict__ P, const float *__restrict__ U, const float *S0, float *bounds,
     float *snap, float *run, int64_t H, int64_t nb)
 {
-    __shared__ __attribute__((aligned(16))) float Ps[kCprD][kCprD];  // 64 KiB
-    __shared__ __attribute__((aligned(16))) float B[kCprPassRows][kCprD];
-    const int64_t h = blockIdx.x;
-    const int r = threadIdx.x >> 5;
-    const int j0 = (threadIdx.x & 31) * 4;
-    const int64_t a = static_cast<int64_t>(blockIdx.y) * kCprPassRows + r;
-    const int64_t row = (h * kCprD + a) * kCprD + j0;  // offset of (h, a, j0) in a state
-    const int64_t state = H * kCprD * kCprD;            // one [H][128][128] block
-    constexpr int kPer = kCprD * kCprD / 4 / kCprThreads;  // float4 of P per thread: 16
-    f32x4 b0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    __shared__ __attribute__((aligned(16))) float Ps[2][kCprD][kCprD];  // 128 KiB
+    __shared__ __attribute__((aligned(16))) float Bs[2][kCprPassRows][kCprD];
+    static_assert(kCprPassRows == 8 && kCprPassThreads == 8 * 64, "one row per wave");
+    const int tid = static_cast<int>(threadIdx.x);
+    const int s = tid >> 6;
+    const int q = tid & 63;
+    const int64_t hs = static_cast<int64_t>(blockIdx.x) * kCprD * kCprD;  // head's state offset
+    const int64_t at = hs + (static_cast<int64_t>(blockIdx.y) * kCprPassRows + s) * kCprD + 2 * q;
+    const int64_t state = H * kCprD * kCprD;  // one [H][128][128] block
+    constexpr int kPer = kCprD * kCprD / 4 / kCprPassThreads;  // float4 of P per thread: 8
+    f32x2 b = f32x2{0.0f, 0.0f};
     if (S0)
-        b0 = *reinterpret_cast<const f32x4 *>(S0 + row);
-    *reinterpret_cast<f32x4 *>(&B[r][j0]) = b0;
+        b = *reinterpret_cast<const f32x2 *>(S0 + at);
+    *reinterpret_cast<f32x2 *>(&Bs[0][s][2 * q]) = b;
     if (bounds)
-        *reinterpret_cast<f32x4 *>(bounds + row) = b0;
+        *reinterpret_cast<f32x2 *>(bounds + at) = b;
     f32x4 pn[kPer];
-    f32x4 un = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x2 un = f32x2{0.0f, 0.0f};
     if (nb > 0) {
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(P + h * kCprD * kCprD);
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(P + hs);
 #pragma unroll
         for (int e = 0; e < kPer; ++e)
-            pn[e] = src[e * kCprThreads + threadIdx.x];
-        un = *reinterpret_cast<const f32x4 *>(U + row);
-    }
-    for (int64_t c = 0; c < nb; ++c) {
-        // P_c into LDS (every lane has finished reading P_{c-1} and B_c is written)
-#pragma unroll
-        for (int e = 0; e < kPer; ++e)
-            reinterpret_cast<f32x4 *>(&Ps[0][0])[e * kCprThreads + threadIdx.x] = pn[e];
-        const f32x4 u = un;
-        __syncthreads();
-        if (c + 1 < nb) {  // next chunk's P and U, in flight during the products
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(P + (c + 1) * state + h * kCprD * kCprD);
+            reinterpret_cast<f32x4 *>(&Ps[0][0][0])[e * kCprPassThreads + tid] =
+                src[e * kCprPassThreads + tid];
+        if (nb > 1) {
+            const f32x4 *nx = reinterpret_cast<const f32x4 *>(P + state + hs);
 #pragma unroll
             for (int e = 0; e < kPer; ++e)
-                pn[e] = src[e * kCprThreads + threadIdx.x];
-            un = *reinterpret_cast<const f32x4 *>(U + (c + 1) * state + row);
+                pn[e] = nx[e * kCprPassThreads + tid];
         }
-        float st[4][7];
-        float root[4];
+        un = *reinterpret_cast<const f32x2 *>(U + at);
+    }
+    __syncthreads();
+    for (int64_t c = 0; c < nb; ++c) {
+        const int cur = static_cast<int>(c & 1);
+        // P_{c+1} into the other buffer (last read in chunk c - 1, before the
+        // barrier), then the loads of P_{c+2} and U_{c+1}: all of it overlaps
+        // this chunk's products.
+        f32x2 un_next = un;
+        if (c + 1 < nb) {
 #pragma unroll
-        for (int m = 0; m < kCprD; ++m) {
-            const float bm = B[r][m];
-            const f32x4 pm = *reinterpret_cast<const f32x4 *>(&Ps[m][j0]);
+            for (int e = 0; e < kPer; ++e)
+                reinterpret_cast<f32x4 *>(&Ps[cur ^ 1][0][0])[e * kCprPassThreads + tid] = pn[e];
+            if (c + 2 < nb) {
+                const f32x4 *nx = reinterpret_cast<const f32x4 *>(P + (c + 2) * state + hs);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < kPer; ++e)
+                    pn[e] = nx[e * kCprPassThreads + tid];
+            }
+            un_next = *reinterpret_cast<const f32x2 *>(U + (c + 1) * state + at);
+        }
+        float st[2][7];
+        float root[2];
+        // Software-pipelined over blocks of 8 terms: the LDS reads of block
+        // k + 1 are in flight while block k is multiplied.  Reads and waits
+        // are inline assembly, so their order is the one written here.
+        const uint32_t pa = lds_addr_of(&Ps[cur][0][2 * q]);
+        const uint32_t ba = lds_addr_of(&Bs[cur][s][0]);
+        f32x2 bq[2][kBlk / 2];
+        f32x4 pq[2][kBlk / 2];
+        pass_block_issue<0>(bq[0], pq[0], pa, ba);
+        static_for<kCprD / kBlk>([&](auto Kc) {
+            constexpr int K = decltype(Kc)::value;
+            constexpr int cb = K & 1;
+            if constexpr (K + 1 < kCprD / kBlk) {
+                pass_block_issue<K + 1>(bq[cb ^ 1], pq[cb ^ 1], pa, ba);
+                lgkm_wait<kBlk>();  // block K landed, block K + 1 may be in flight
+            } else {
+                lgkm_wait<0>();
+            }
+#pragma unroll
+            for (int i = 0; i < kBlk / 2; ++i) {
+                lds_pin(bq[cb][i]);
+                lds_pin(pq[cb][i]);
+            }
+#pragma unroll
+            for (int i = 0; i < kBlk; ++i) {
+                const int m = K * kBlk + i;
                 // binary counter over the 128 products: the trailing ones of
                 // m are the saved left siblings this product closes
                 const int ones = __builtin_ctz(~static_cast<unsigned>(m));
-                float x = bm * pm[e];
-                for (int lvl = 0; lvl < ones; ++lvl)
-                    x = st[e][lvl] + x;
-                if (ones < 7)
-                    st[e][ones] = x;
-                else
-                    root[e] = x;
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    float x = bq[cb][i >> 1][i & 1] * pq[cb][i >> 1][2 * (i & 1) + cc];
+                    for (int lvl = 0; lvl < ones; ++lvl)
+                        x = st[cc][lvl] + x;
+                    if (ones < 7)
+                        st[cc][ones] = x;
+                    else
+                        root[cc] = x;
+                }
             }
-        }
-        const f32x4 nxt = f32x4{u[0] + root[0], u[1] + root[1], u[2] + root[2], u[3] + root[3]};
-        __syncthreads();  // every lane has read B_c and P_c
-        *reinterpret_cast<f32x4 *>(&B[r][j0]) = nxt;
+        });
+        b = f32x2{un[0] + root[0], un[1] + root[1]};
+        *reinterpret_cast<f32x2 *>(&Bs[cur ^ 1][s][2 * q]) = b;
         if (bounds)
-            *reinterpret_cast<f32x4 *>(bounds + (c + 1) * state + row) = nxt;
+            *reinterpret_cast<f32x2 *>(bounds + (c + 1) * state + at) = b;
+        un = un_next;
+        lds_barrier();  // the loads of P_{c+2} stay in flight
     }
-    __syncthreads();
-    const f32x4 fin = *reinterpret_cast<const f32x4 *>(&B[r][j0]);
-    *reinterpret_cast<f32x4 *>(snap + row) = fin;
+    *reinterpret_cast<f32x2 *>(snap + at) = b;
     if (run)
-        *reinterpret_cast<f32x4 *>(run + row) = fin;
+        *reinterpret_cast<f32x2 *>(run + at) = b;
 }
 
 // One decode step of token `pos` for every head: the running state run
@@ -344,7 +434,7 @@ hipError_t launch_cpr_prefill(const uint16_t *q, const uint16_t *k, const uint16
         hipLaunchKernelGGL(cpr_transition_kernel, dim3(static_cast<unsigned>(H), static_cast<unsigned>(nb)),
                            dim3(kCprThreads), 0, stream, k, v, alpha, beta, P, U, int64_t{0}, H, C);
     hipLaunchKernelGGL(cpr_pass_kernel, dim3(static_cast<unsigned>(H), kCprD / kCprPassRows),
-                       dim3(kCprThreads), 0, stream, P, U, S0, bounds, snap,
+                       dim3(kCprPassThreads), 0, stream, P, U, S0, bounds, snap,
                        (T % C == 0) ? run : nullptr, H, nb);
     if (nchunks > 0)
         hipLaunchKernelGGL(cpr_output_kernel, dim3(static_cast<unsigned>(H), static_cast<unsigned>(nchunks)),
@@ -364,7 +454,7 @@ hipError_t launch_cpr_decode(const uint16_t *q, const uint16_t *k, const uint16_
         hipLaunchKernelGGL(cpr_transition_kernel, dim3(static_cast<unsigned>(H), 1u), dim3(kCprThreads), 0,
                            stream, k, v, alpha, beta, P, U, pos - (C - 1), H, C);
         hipLaunchKernelGGL(cpr_pass_kernel, dim3(static_cast<unsigned>(H), kCprD / kCprPassRows),
-                           dim3(kCprThreads), 0, stream, P, U, snap, static_cast<float *>(nullptr),
+                           dim3(kCprPassThreads), 0, stream, P, U, snap, static_cast<float *>(nullptr),
                            snap, run, H, int64_t{1});
     }
     return hipGetLastError();

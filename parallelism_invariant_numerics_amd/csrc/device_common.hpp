@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace iso {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -16,6 +18,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(static_cast<F &&>(f), std::make_integer_sequence<int, N>{});
+}
+
 
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b)
@@ -96,6 +112,14 @@ __device__ __forceinline__ float row16_max(float m)
     m = fmaxf(m, dpp_mov<0x141>(m));
     m = fmaxf(m, dpp_mov<0x140>(m));
     return m;
+}
+
+// Workgroup barrier for code that has global loads in flight which the
+// barrier must not wait for (__syncthreads() may also drain the vector
+// memory counter): LDS operations complete first, then all waves meet.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace iso

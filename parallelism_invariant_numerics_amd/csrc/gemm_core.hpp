@@ -160,18 +160,6 @@ __device__ __forceinline__ int lane_id()
     return l;
 }
 
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
-{
-    (f(std::integral_constant<int, I>{}), ...);
-}
-
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    static_for_impl(static_cast<F &&>(f), std::make_integer_sequence<int, N>{});
-}
-
 // ------------------------------------------------------------------ sources
 
 // A 128-row operand tile: rows [0, rows) of a k-contiguous matrix starting at
@@ -567,14 +555,6 @@ template <class T>
 __device__ __forceinline__ void lds_pin(T &v)
 {
     asm volatile("" : "+v"(v));
-}
-
-// Workgroup barrier for code that has global loads in flight which the
-// barrier must not wait for (__syncthreads() may also drain the vector
-// memory counter): LDS operations complete first, then all waves meet.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Fixed tree over P partition roots (P = 1, 2, 4, 8), lower index left.
