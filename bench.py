@@ -35,9 +35,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-# FP32 vector operations without FMA or packed pairs: 256 CUs x 4 SIMDs x 16
-# lanes x 2.4 GHz (the 157.3 TFLOP/s figure counts FMA and packed FP32 twice each)
-PEAK_FP32_OPS_T = 39.3
+# FP32 vector operations (one multiply or one add, no FMA, no packed pairs):
+# 256 CUs x 128 FP32 lanes per clock x 2.4 GHz; the 157.3 TFLOP/s vector figure
+# counts an FMA as two.  Independent v_add_f32 / v_mul_f32 measure ~71 T/s at
+# the loaded clock with four waves per SIMD, ~49 T/s with one.
+PEAK_FP32_OPS_T = 78.6
 
 
 def _args():
