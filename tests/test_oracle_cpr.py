@@ -208,3 +208,24 @@ def test_rejects_bad_arguments():
         oracle.cpr_prefill(y["q"], y["k"][:3], y["v"], y["alpha"], y["beta"], 2)
     with pytest.raises(ValueError):
         oracle.cpr_prefill(y["q"], y["k"], y["v"], y["alpha"], y["beta"], 0)
+
+
+def test_dot_products_are_balanced_trees():
+    """The output dot product of one token with beta = 0, alpha = 1 (the state
+    is unchanged) over the products [2^24, 1, 1, -2^24]: the balanced tree
+    gives (2^24 + 1) + (1 - 2^24) = 2^24 + (1 - 2^24) = 1 in FP32 (2^24 + 1
+    rounds to 2^24), a left-to-right sum gives 0 and a right-to-left sum 2.
+    Every CPR dot product (step, chunk form, pass) is this one tree."""
+    d = 4
+    S0 = np.zeros((1, d, d), dtype=np.float32)
+    S0[0, 0] = [2.0 ** 24, 1.0, 1.0, -(2.0 ** 24)]
+    S0[0, 1] = [-(2.0 ** 24), 1.0, 1.0, 2.0 ** 24]  # tree 1, left-to-right 2, right-to-left 0
+    q = _bits(np.ones((1, 1, d)))
+    k = _bits(np.full((1, 1, d), 0.5))
+    v = _bits(np.zeros((1, 1, d)))
+    one = np.ones((1, 1), dtype=np.float32)
+    zero = np.zeros((1, 1), dtype=np.float32)
+    o, _, run = oracle.cpr_prefill(q, k, v, one, zero, 4, S0=S0)
+    assert o[0, 0, 0] == 1.0
+    assert o[0, 0, 1] == 1.0
+    assert np.array_equal(run, S0)
