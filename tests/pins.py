@@ -85,7 +85,7 @@ def f32_bits(x) -> np.ndarray:
 
 def rmsnorm_pins():
     """Rows of rmsnorm_pins.txt grouped by kind."""
-    out = {"ss": [], "add": [], "y": []}
+    out = {"ss": [], "add": [], "y": [], "row": []}
     for row in _lines("rmsnorm_pins.txt"):
         kind = row[0]
         if kind == "ss":
@@ -98,6 +98,11 @@ def rmsnorm_pins():
             out["y"].append(dict(H=int(row[1]), L=int(row[2]), h=int(row[3], 16),
                                  w=int(row[4], 16), eps=float(row[5]),
                                  y_bf16=int(row[6], 16), y_f32=int(row[7], 16)))
+        elif kind == "row":
+            out["row"].append(dict(H=int(row[1]), L=int(row[2]), eps=float(row[3]),
+                                   h=[int(v, 16) for v in row[4].split()],
+                                   w=[int(v, 16) for v in row[5].split()],
+                                   y_f32=[int(v, 16) for v in row[6].split()]))
     return out
 
 

@@ -43,6 +43,16 @@ def test_closed_form_rows(pin):
     assert np.all(yf.view(np.uint32) == pin["y_f32"])
 
 
+@pytest.mark.parametrize("pin", PINS["row"], ids=lambda p: f"H{p['H']}L{p['L']}")
+def test_hand_worked_rows(pin):
+    """FP32 outputs of hand-derived rows: fixes where eps sits and the
+    association (h * r) * w of the last step."""
+    x = np.array([pin["h"]], dtype=np.uint16)
+    w = np.array(pin["w"], dtype=np.uint16)
+    yf, _, _ = oracle.rmsnorm(x, w, pin["L"], pin["eps"], out_bf16=False)
+    assert np.array_equal(yf.view(np.uint32)[0], np.array(pin["y_f32"], dtype=np.uint32))
+
+
 @pytest.mark.parametrize("H,L,eps", [(2048, 64, 1e-6), (2048, 1, 1e-6), (2048, 2048, 1e-6),
                                      (512, 16, 0.25), (4096, 256, 1e-6), (256, 32, 3.0)])
 def test_against_float64_definition(H, L, eps):
