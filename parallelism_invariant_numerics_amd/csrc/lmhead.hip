@@ -158,10 +158,13 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
             const int64_t rel = t - n0 - wc * WCOLS - (lane & 15);
             if (rel >= 0 && rel < WCOLS && (rel & 15) == 0 && t < a.V) {
                 const int j = static_cast<int>(rel >> 4);
+                // a select chain: an indexed read of z would put the tile in
+                // private memory
+                float zt = z.v[i][0][r];
 #pragma unroll
-                for (int jj = 0; jj < C::JB; ++jj)
-                    if (jj == j)
-                        a.target[row] = z.v[i][jj][r];
+                for (int jj = 1; jj < C::JB; ++jj)
+                    zt = j == jj ? z.v[i][jj][r] : zt;
+                a.target[row] = zt;
             }
         }
 }

@@ -44,7 +44,7 @@ def test_uniform_logits(V):
 
 
 @pytest.mark.parametrize("M,V,K,L", [(1, 1000, 256, 4), (130, 4099, 512, 8), (3, 127, 256, 2),
-                                     (257, 129, 1024, 16), (5, 2000, 2048, 32)])
+                                     (257, 129, 1024, 16), (5, 2000, 2048, 32), (9, 300, 256, 1)])
 def test_ragged_parity(M, V, K, L):
     H = normal_bf16(M + 3, (M, K), 1.0)
     Wvt = normal_bf16(V + 4, (V, K), 0.05)
