@@ -169,13 +169,21 @@ __device__ __forceinline__ void chunk_stats_epilogue(const Acc<C> &z, int64_t m0
         }
 }
 
-// Origin and operand pipe of tile t of the grouped order.
+// Tile order of the LM-head: groups of kLmColGroup vocabulary tiles, tile
+// columns fastest inside a group, then the next row tile.  Each XCD takes a
+// contiguous stretch of this order, i.e. its own eighth of the vocabulary for
+// every row, so the 622 MB vocabulary matrix streams through one L2 instead
+// of all eight, and only the hidden rows (34 MB) are shared.  The 32 tiles
+// that run together on an XCD are 4 vocabulary tiles x 8 row tiles.
+constexpr int kLmColGroup = 4;
+
+// Origin and operand pipe of tile t of that order.
 template <class C>
 __device__ __forceinline__ Pipe lm_tile(const LmArgs &a, int t, int tm, int tn, int64_t &m0,
                                         int64_t &n0)
 {
     int mt, nt;
-    grouped_tile(t, tm, tn, 8, mt, nt);
+    grouped_tile(t, tn, tm, kLmColGroup, nt, mt);
     m0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(mt)) * BM;
     n0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(nt)) * BN;
     return make_pipe<C>(a.H + m0 * a.K, a.M - m0, a.Wvt + n0 * a.K, a.V - n0, a.K, 0);
@@ -199,9 +207,9 @@ __device__ __forceinline__ void tok_dma(const LmArgs &a, int64_t m0, int32_t *ds
 }
 
 // Persistent: the workgroups on XCD x take the contiguous range
-// [x per, (x+1) per) of the grouped tile order (so the tiles running together
-// on one L2 share hidden rows and vocabulary rows), stepping by the number of
-// workgroups per XCD.  The next tile's first stages and token ids are
+// [x per, (x+1) per) of the LM-head tile order (so the tiles running together
+// on one L2 share hidden rows and vocabulary rows, and each vocabulary tile is
+// needed by one XCD only), stepping by the number of workgroups per XCD.  The next tile's first stages and token ids are
 // requested before the current tile's softmax epilogue, which hides their
 // latency.  Nothing but loads to LDS is in flight across the epilogue, and
 // nothing is carried in vector registers from one tile to the next.
