@@ -257,6 +257,224 @@ __global__ __launch_bounds__(C::kThreads, 2) void lmhead_fused_kernel(LmArgs a)
     }
 }
 
+// ------------------------------------------------------ decode (M <= 16 rows)
+//
+// A decode step evaluates one to 16 rows against the whole vocabulary: the
+// 622 MB vocabulary matrix is read once and the rows fill a single 16-row
+// MFMA block.  The work is the same as the fused kernel's for those rows (the
+// same v_mfma_f32_16x16x32_bf16 chain per leaf in ascending k, the same
+// balanced tree over the leaves, the same chunk statistics), so the bits are
+// those of the fused kernel; only the data movement differs.  One workgroup
+// of 16 waves per CU walks the chunks (128 vocabulary ids each) in a
+// grid-stride loop.  Wave w takes the 16 ids n0 + 16 (w & 7) .. + 15 and the
+// leaves of half w >> 3 of the leaf block (a subtree of 2^(LOG-1) leaves);
+// the two half roots are added in the epilogue, the top tree level.  Weight
+// fragments go from HBM straight to registers, one leaf (KS k-steps) ahead,
+// so a CU keeps 16 x KS KiB of weights in flight; the rows (zero past M) sit
+// in LDS for the whole launch.  The chunk statistics use the balanced tree
+// over the eight 16-id blocks in id order, which is the fused kernel's tree.
+constexpr int kDecRows = 16;
+constexpr int kDecWaves = 16;
+constexpr int64_t kDecMaxK = 4096;
+constexpr int kDecPitchMax = static_cast<int>(kDecMaxK) * 2 + 16;  // LDS bytes per row
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v)
+{
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int LOG, int KS>
+__global__ __launch_bounds__(kDecWaves * 64) void lmhead_decode_kernel(LmArgs a)
+{
+    static_assert(LOG >= 2, "two halves of at least two leaves");
+    constexpr int LH = 1 << (LOG - 1);  // leaves per half (even)
+    __shared__ __attribute__((aligned(16))) char arow[kDecRows * kDecPitchMax];
+    __shared__ __attribute__((aligned(16))) f32x4 xroot[8][64];
+    __shared__ float red_m[8][kDecRows], red_s[8][kDecRows];
+
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int blk = wave & 7, half = wave >> 3;
+    const int64_t K = a.K;
+    const int pitch = static_cast<int>(K) * 2 + 16;  // 16 bytes of padding: rows shift banks
+
+    // the rows into LDS (rows M .. 15 zero), 16 bytes per thread and step
+    {
+        const int per_row = static_cast<int>(K / 8);
+        for (int q = threadIdx.x; q < kDecRows * per_row; q += kDecWaves * 64) {
+            const int r = q / per_row, c = q % per_row;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (r < a.M)
+                v = *reinterpret_cast<const u32x4 *>(a.H + static_cast<int64_t>(r) * K + 8 * c);
+            *reinterpret_cast<u32x4 *>(arow + r * pitch + 16 * c) = v;
+        }
+    }
+    __syncthreads();
+
+    int64_t c = blockIdx.x;
+    if (c >= a.nchunk)
+        return;  // the whole workgroup
+    // this lane's A fragment row (lane & 15) and k-group (lane >> 4); its B
+    // row (lane & 15) of the wave's 16 ids and the same k-group
+    const uint32_t a_lds = lds_addr(arow) + static_cast<uint32_t>((lane & 15) * pitch + (lane >> 4) * 16);
+    const uint32_t voff = static_cast<uint32_t>((lane & 15) * K * 2 + (lane >> 4) * 16);
+    const int kstep0 = half * LH * KS;  // this half's first k-step
+
+    auto brsrc = [&](int64_t ch) {
+        const int64_t col0 = ch * kChunk + 16 * blk;
+        int64_t rows = a.V - col0;
+        rows = rows < 0 ? 0 : (rows > 16 ? 16 : rows);
+        return tile_rsrc(a.Wvt + (rows > 0 ? col0 : 0) * K, rows, K);
+    };
+    auto load_leaf = [&](u32x4 (&dst)[KS], __amdgpu_buffer_rsrc_t r, int leaf) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            dst[kk] = __builtin_amdgcn_raw_buffer_load_b128(
+                r, voff, static_cast<int>((kstep0 + leaf * KS + kk) * 64), 0);
+    };
+
+    u32x4 bb[2][KS];
+    __amdgpu_buffer_rsrc_t rb = brsrc(c);
+    load_leaf(bb[0], rb, 0);
+    for (;;) {
+        const int64_t cn = c + gridDim.x;
+        const __amdgpu_buffer_rsrc_t rbn = brsrc(cn < a.nchunk ? cn : c);
+        f32x4 stk[LOG - 1];
+        f32x4 acc;
+        static_for<LH>([&](auto Jc) {
+            constexpr int J = decltype(Jc)::value;
+            constexpr int cur = J & 1;
+            // the next leaf of this chunk, or leaf 0 of the next chunk (LH is
+            // even, so that one lands in buffer 0)
+            if constexpr (J + 1 < LH)
+                load_leaf(bb[cur ^ 1], rb, J + 1);
+            else if (cn < a.nchunk)
+                load_leaf(bb[cur ^ 1], rbn, 0);
+            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                f32x4 av;
+                lds_issue_b128(av, a_lds + static_cast<uint32_t>((kstep0 + J * KS + kk) * 64));
+                lds_wait();
+                lds_pin(av);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                              as_bf16x8(bb[cur][kk]), acc, 0, 0, 0);
+            }
+            // binary-counter tree over the half's leaves (lower leaves left)
+            bool done = false;
+#pragma unroll
+            for (int b = 0; b < LOG - 1; ++b) {
+                if (!done) {
+                    if ((J >> b) & 1) {
+                        acc = stk[b] + acc;
+                    } else {
+                        stk[b] = acc;
+                        done = true;
+                    }
+                }
+            }
+        });
+
+        // epilogue: z = (first half) + (second half), then the chunk statistics
+        if (half == 1)
+            xroot[blk][lane] = acc;
+        lds_barrier();
+        const int64_t n0 = c * kChunk;
+        const int64_t col = n0 + 16 * blk + (lane & 15);
+        const bool colv = col < a.V;
+        f32x4 z = acc;
+        if (half == 0) {
+            z = acc + xroot[blk][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float m = colv ? z[r] : -INFINITY;
+                m = row16_max(m);
+                if ((lane & 15) == 0)
+                    red_m[blk][4 * (lane >> 4) + r] = m;
+            }
+        }
+        lds_barrier();
+        if (half == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * (lane >> 4) + r;
+                float cm = red_m[0][row];
+#pragma unroll
+                for (int q = 1; q < 8; ++q)
+                    cm = fmaxf(cm, red_m[q][row]);
+                const float e = colv ? exp_neg(z[r] - cm) : 0.0f;
+                const float sblk = row16_sum(e);
+                if ((lane & 15) == 0)
+                    red_s[blk][row] = sblk;
+                if (row < a.M) {
+                    const int64_t t = static_cast<int64_t>(a.tok[row]) - a.v0;
+                    if (t == col && t < a.V)
+                        a.target[row] = z[r];
+                }
+            }
+        }
+        lds_barrier();
+        if (wave == 0 && (lane & 15) == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * (lane >> 4) + r;
+                if (row < a.M) {
+                    float cm = red_m[0][row];
+#pragma unroll
+                    for (int q = 1; q < 8; ++q)
+                        cm = fmaxf(cm, red_m[q][row]);
+                    const float sum = ((red_s[0][row] + red_s[1][row]) + (red_s[2][row] + red_s[3][row])) +
+                                      ((red_s[4][row] + red_s[5][row]) + (red_s[6][row] + red_s[7][row]));
+                    float *st = a.stats + (row * a.stats_stride + a.chunk0 + c) * 2;
+                    st[0] = cm;
+                    st[1] = sum;
+                }
+            }
+        }
+        if (cn >= a.nchunk)
+            break;
+        c = cn;
+        rb = rbn;
+    }
+}
+
+template <int LOG, int KS>
+static hipError_t launch_decode(const LmArgs &a, hipStream_t stream)
+{
+    int64_t g = device_cus();
+    g = a.nchunk < g ? a.nchunk : g;
+    hipLaunchKernelGGL((lmhead_decode_kernel<LOG, KS>), dim3(static_cast<unsigned>(g)),
+                       dim3(kDecWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+// The decode kernel when it applies (one partition, M <= 16, four or eight
+// leaves of 64, 128 or 256 columns, K <= 4096); hipErrorNotSupported
+// otherwise (the fused kernel takes those).
+static hipError_t try_decode(const LmArgs &a, int leaves, int leaf_size, hipStream_t stream)
+{
+    if (a.M < 1 || a.M > kDecRows || a.K > kDecMaxK)
+        return hipErrorNotSupported;
+    const int ks = leaf_size / 32;
+    if (leaves == 4) {
+        switch (ks) {
+        case 2: return launch_decode<2, 2>(a, stream);
+        case 4: return launch_decode<2, 4>(a, stream);
+        case 8: return launch_decode<2, 8>(a, stream);
+        default: return hipErrorNotSupported;
+        }
+    }
+    if (leaves == 8) {
+        switch (ks) {
+        case 2: return launch_decode<3, 2>(a, stream);
+        case 4: return launch_decode<3, 4>(a, stream);
+        case 8: return launch_decode<3, 8>(a, stream);
+        default: return hipErrorNotSupported;
+        }
+    }
+    return hipErrorNotSupported;
+}
+
 // Several partitions: fold the partition roots of the logits with the top
 // tree levels, in the MFMA layout, then the same epilogue.
 template <int P>
@@ -388,6 +606,9 @@ hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int
     a.stats_stride = (v_total + kChunk - 1) / kChunk;
     a.stages_per_leaf = leaf_size / BK;
     if (parts == 1) {
+        const hipError_t d = try_decode(a, leaves_per_part, leaf_size, stream);
+        if (d != hipErrorNotSupported)
+            return d;
         switch (leaves_per_part) {
         case 1: return launch_fused<0>(a, stream);
         case 2: return launch_fused<1>(a, stream);

@@ -105,3 +105,26 @@ def test_lmhead_full_size_sampled():
     small = _lp(H[rows], None, tok[rows], L, 1, dW)
     assert np.array_equal(u32(small), u32(got[rows]))
     assert np.all(np.isfinite(got)) and np.all(got <= 0)
+
+
+@pytest.mark.parametrize("K,L,V", [(256, 4, 1000), (512, 4, 77), (512, 8, 1200), (1024, 8, 300),
+                                   (2048, 8, 5000), (4096, 8, 700)])
+def test_decode_rows_match_batch(K, L, V):
+    """One to 16 rows take the decode kernel (weights streamed to registers, one workgroup per
+    CU); the same rows inside a batch of 40 take the fused kernel.  Same bits, ragged and
+    sub-chunk vocabularies, bad token ids, and leaf sizes the decode kernel does not take."""
+    H = normal_bf16(K + V, (40, K), 1.0)
+    Wvt = normal_bf16(K + V + 1, (V, K), 0.05)
+    tok = uniform_tokens(K + 2, 40, V)
+    tok[3], tok[5], tok[21] = V - 1, -1, V
+    dW = dev(Wvt)
+    note(f"decode rows vs batch K={K} L={L} V={V}")
+    big = _lp(H, None, tok, L, 1, dW)
+    for m in (1, 7, 16):
+        for start in (0, 20):
+            small = _lp(H[start:start + m], None, tok[start:start + m], L, 1, dW)
+            assert np.array_equal(u32(small), u32(big[start:start + m])), (m, start)
+    want, _, _ = oracle.lmhead_logprob(H[:16], Wvt, tok[:16], L)
+    ok = np.isfinite(want)
+    assert np.array_equal(ok, np.isfinite(big[:16]))
+    assert np.max(np.abs(big[:16][ok] - want[ok])) <= LOGPROB_ATOL
