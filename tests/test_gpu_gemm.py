@@ -133,3 +133,18 @@ def test_baseline_accuracy():
     out = iso.gemm_baseline(dev(A), dev(Wt))
     torch().cuda.synchronize()
     check_gemm_tol(host(out), oracle.gemm(A, Wt, 8), absdot(A, Wt), "baseline")
+
+
+@pytest.mark.parametrize("M,N", [(65, 257), (64, 256), (3, 5)])
+def test_partition_combine_shapes(M, N):
+    """The combine of the partition roots on odd, aligned and tiny M N gives the P = 1 bits,
+    FP32 and bf16 (the P = 8 workspace of these shapes included)."""
+    K, L = 2048, 8
+    A = normal_bf16(M + 31, (M, K), 1.0)
+    Wt = normal_bf16(N + 32, (N, K), 0.02)
+    note(f"partition combine shapes M={M} N={N}")
+    base = u32(_run(A, Wt, L, 1))
+    for P in (2, 4, 8):
+        assert np.array_equal(u32(_run(A, Wt, L, P)), base), P
+        bf = _run(A, Wt, L, P, iso.BF16)
+        assert np.array_equal(bf, f32_to_bf16_bits(base.view(np.float32))), P
