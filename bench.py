@@ -263,7 +263,16 @@ def main():
                           "p1_tflops": round(fs / (ms1 * 1e-3) / 1e12, 2),
                           "p8_tflops": round(fs / (ms8 * 1e-3) / 1e12, 2),
                           "p1_ms": round(ms1, 4), "p8_ms": round(ms8, 4)}
-        del Ws, As, outs, ws8, ref_s
+        # one row per call (a decode step of the same layer): the weights streamed once
+        A1 = As[:1].contiguous()
+        o1 = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
+        g_1 = lambda: iso.gemm(A1, Ws, cs, out=o1)
+        g_1()
+        ms_1 = _time_events(g_1, max(10, args.steps), stream)
+        ok &= bool(torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
+        extra["sweep"]["row1_us"] = round(ms_1 * 1e3, 2)
+        extra["sweep"]["row1_weight_gbs"] = round(4096 * Ks * 2 / (ms_1 * 1e-3) / 1e9, 1)
+        del Ws, As, outs, ws8, ref_s, A1, o1
 
         # ---------------- LM-head logprob
         lm = make_config("lmhead")

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libiso.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["gemm.hip", "lmhead.hip", "moe.hip", "norm.hip", "cpr.hip"]
+DEVICE_SOURCES = ["gemm.hip", "gemm_rows.hip", "lmhead.hip", "moe.hip", "norm.hip", "cpr.hip"]
 HOST_SOURCES = ["iso_host.cpp", "sha256.cpp", "identity.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++20", "-Wall", "-I", os.path.join(ROOT, "include")]

@@ -230,6 +230,13 @@ iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lpp = (int)c->leaf_count / parts;
     const int bf16 = out_dtype == ISO_BF16;
+    if (partitions == 1) {  // a few rows: the weight-streaming kernel, same bits
+        const hipError_t r = iso::launch_gemm_rows(
+            static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Wt), C, bf16, M, N, K,
+            (int)c->leaf_count, (int)c->leaf_size, st);
+        if (r != hipErrorNotSupported)
+            return launch_status(r);
+    }
     if (parts == 1)
         return launch_status(iso::launch_gemm_partials(
             static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Wt), C, bf16 ? 1 : 0,

@@ -148,3 +148,24 @@ def test_partition_combine_shapes(M, N):
         assert np.array_equal(u32(_run(A, Wt, L, P)), base), P
         bf = _run(A, Wt, L, P, iso.BF16)
         assert np.array_equal(bf, f32_to_bf16_bits(base.view(np.float32))), P
+
+
+@pytest.mark.parametrize("K,L,N", [(256, 4, 300), (512, 4, 128), (2048, 8, 2048), (1024, 8, 77),
+                                   (4096, 16, 4096), (2048, 32, 130), (4096, 64, 96),
+                                   (4096, 8, 256)])
+def test_few_rows_match_batch(K, L, N):
+    """One to 16 rows take the weight-streaming kernel (one workgroup per 16 output columns,
+    eight subtrees of leaves per column block); the same rows inside a batch of 200 take the
+    tile kernel.  Same bits, FP32 and bf16, ragged N, and a leaf size it does not take."""
+    A = normal_bf16(K + N, (200, K), 1.0)
+    Wt = normal_bf16(K + N + 1, (N, K), 0.02)
+    note(f"few rows vs batch K={K} L={L} N={N}")
+    big = u32(_run(A, Wt, L))
+    bigb = _run(A, Wt, L, 1, iso.BF16)
+    for m in (1, 5, 16):
+        for start in (0, 150):
+            assert np.array_equal(u32(_run(A[start:start + m], Wt, L)), big[start:start + m]), (m, start)
+            assert np.array_equal(_run(A[start:start + m], Wt, L, 1, iso.BF16),
+                                  bigb[start:start + m]), (m, start)
+    check_gemm_tol(big[:16].view(np.float32), oracle.gemm(A[:16], Wt, L), absdot(A[:16], Wt),
+                   f"few rows {K}/{L}")
