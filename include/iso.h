@@ -223,6 +223,9 @@ size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int parti
  * `partitions` P emulates P tensor-parallel ranks on this GPU: partition p
  * computes its subtree root into the workspace and a combine kernel applies
  * the top log2(P) levels.  Every P allowed by the claim gives the same bits.
+ * The launch shape follows the problem (128 x 128 tiles; with P = 1 and at
+ * most 16 rows, one workgroup per 16 output columns streaming the weights),
+ * never the numbers: a row's bits do not depend on M or on its position.
  * Limits: M, N < 2^23 and (M/128)(N/128) < 2^28 tiles, K <= 2^22.
  */
 iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *C,
@@ -255,7 +258,9 @@ size_t iso_lmhead_workspace(const iso_contract *c, int64_t M, int64_t V, int par
  * pairs (m, s) are merged over the balanced tree in chunk order (padded with
  * the identity (-inf, 0)) by (m, s) + (m', s') = (u, s e^(m-u) + s' e^(m'-u)),
  * u = max(m, m').  c->vocab_chunk must be ISO_VOCAB_CHUNK.  A token id
- * outside [0, V) gives NaN for its row.  Limits: 1 <= V <= 2^20, M < 2^31.
+ * outside [0, V) gives NaN for its row.  Up to 16 rows (one partition) run a
+ * decode kernel that streams the vocabulary matrix once; the bits are those
+ * of the same rows in any larger batch.  Limits: 1 <= V <= 2^20, M < 2^31.
  */
 iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *Wvt,
                               const int32_t *tok, float *logprob, int64_t M, int64_t V,
