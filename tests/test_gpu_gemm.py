@@ -152,11 +152,12 @@ def test_partition_combine_shapes(M, N):
 
 @pytest.mark.parametrize("K,L,N", [(256, 4, 300), (512, 4, 128), (2048, 8, 2048), (1024, 8, 77),
                                    (4096, 16, 4096), (2048, 32, 130), (4096, 64, 96),
-                                   (4096, 8, 256)])
+                                   (4096, 8, 256), (4096, 4, 256), (1024, 2, 200)])
 def test_few_rows_match_batch(K, L, N):
     """One to 16 rows take the weight-streaming kernel (one workgroup per 16 output columns,
     eight subtrees of leaves per column block); the same rows inside a batch of 200 take the
-    tile kernel.  Same bits, FP32 and bf16, ragged N, and a leaf size it does not take."""
+    tile kernel.  Same bits, FP32 and bf16, ragged N; 4 leaves of 1024 and 2 leaves are shapes
+    it leaves to the tile kernels."""
     A = normal_bf16(K + N, (200, K), 1.0)
     Wt = normal_bf16(K + N + 1, (N, K), 0.02)
     note(f"few rows vs batch K={K} L={L} N={N}")
