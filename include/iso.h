@@ -224,7 +224,7 @@ size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int parti
  * computes its subtree root into the workspace and a combine kernel applies
  * the top log2(P) levels.  Every P allowed by the claim gives the same bits.
  * The launch shape follows the problem (128 x 128 tiles; with P = 1 and at
- * most 16 rows, one workgroup per 16 output columns streaming the weights),
+ * most 32 rows, one workgroup per 16 output columns streaming the weights),
  * never the numbers: a row's bits do not depend on M or on its position.
  * Limits: M, N < 2^23 and (M/128)(N/128) < 2^28 tiles, K <= 2^22.
  */

@@ -1,4 +1,4 @@
-// gemm_rows.hip -- the leaf/tree GEMM for calls of at most 16 rows (decode
+// gemm_rows.hip -- the leaf/tree GEMM for calls of at most 32 rows (decode
 // steps of a linear layer), for gfx950.
 //
 // Numerics: those of gemm_core.hpp ("IsoExec: Eliminating Trainer-Inference
@@ -8,23 +8,24 @@
 // started from +0.0, and the leaves are combined by the same balanced tree,
 // so an element has the bits the tile kernels give it in any batch.
 //
-// Why a kernel of its own: with one to 16 rows the work is the weight
+// Why a kernel of its own: with one to 32 rows the work is the weight
 // stream (N x K bf16), and a 128 x 128 output tile per workgroup leaves all
 // but N / 128 CUs idle.  Here a workgroup of eight waves takes 16 output
 // columns (two blocks of 16 for four leaves); wave w of a block takes the
 // contiguous subtree of L / S leaves number w (S = 8, or 4 for four
 // leaves), loads all of its weight and row fragments into registers at once,
-// and folds its leaves with the register tree.  The S subtree roots meet in
-// LDS, where the top log2 S tree levels combine them in index order.
+// and folds its leaves with the register tree, one accumulator per 16-row
+// MFMA block (two above 16 rows).  The S subtree roots meet in LDS, where the
+// top log2 S tree levels combine them in index order.
 #include "gemm_core.hpp"
 #include "kernels.h"
 
 namespace iso {
 
-constexpr int kRowsMax = 16;
+constexpr int kRowsMax = 32;  // two 16-row MFMA blocks
 constexpr int64_t kRowsMaxK = 4096;
 
-template <int S, int LWLOG, int KS>
+template <int S, int LWLOG, int KS, int RB>
 __global__ __launch_bounds__(512) void gemm_rows_kernel(const uint16_t *A, const uint16_t *Wt,
                                                         void *out, int out_bf16, int64_t M,
                                                         int64_t N, int64_t K)
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(512) void gemm_rows_kernel(const uint16_t *A, const
     constexpr int LW = 1 << LWLOG;  // leaves per wave
     constexpr int NK = LW * KS;     // k-steps (32 columns of K) per wave
     constexpr int BPW = 8 / S;      // 16-column blocks per workgroup
-    __shared__ __attribute__((aligned(16))) f32x4 roots[8][64];
+    __shared__ __attribute__((aligned(16))) f32x4 roots[RB][8][64];
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -49,59 +50,70 @@ __global__ __launch_bounds__(512) void gemm_rows_kernel(const uint16_t *A, const
     const uint32_t voff = static_cast<uint32_t>((lane & 15) * K * 2 + (lane >> 4) * 16);
     const int k0 = sub * NK;
 
-    u32x4 af[NK], bf[NK];
+    u32x4 af[RB][NK], bf[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
         bf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, (k0 + kk) * 64, 0);
-        af[kk] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff, (k0 + kk) * 64, 0);
+#pragma unroll
+        for (int q = 0; q < RB; ++q)  // row block q: rows 16 q .. 16 q + 15
+            af[q][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, voff + static_cast<uint32_t>(16 * q * K * 2), (k0 + kk) * 64, 0);
     }
 
-    f32x4 stk[LWLOG > 0 ? LWLOG : 1];
-    f32x4 acc;
+    f32x4 stk[RB][LWLOG > 0 ? LWLOG : 1];
+    f32x4 acc[RB];
     static_for<LW>([&](auto Jc) {
         constexpr int J = decltype(Jc)::value;
-        acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, af[J * KS + kk]),
-                __builtin_bit_cast(bf16x8, bf[J * KS + kk]), acc, 0, 0, 0);
-        // binary-counter tree over the wave's leaves (lower leaves left)
-        bool done = false;
+        for (int q = 0; q < RB; ++q) {
+            acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int b = 0; b < LWLOG; ++b) {
-            if (!done) {
-                if ((J >> b) & 1) {
-                    acc = stk[b] + acc;
-                } else {
-                    stk[b] = acc;
-                    done = true;
+            for (int kk = 0; kk < KS; ++kk)
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, af[q][J * KS + kk]),
+                    __builtin_bit_cast(bf16x8, bf[J * KS + kk]), acc[q], 0, 0, 0);
+            // binary-counter tree over the wave's leaves (lower leaves left)
+            bool done = false;
+#pragma unroll
+            for (int b = 0; b < LWLOG; ++b) {
+                if (!done) {
+                    if ((J >> b) & 1) {
+                        acc[q] = stk[q][b] + acc[q];
+                    } else {
+                        stk[q][b] = acc[q];
+                        done = true;
+                    }
                 }
             }
         }
     });
 
-    roots[wave][lane] = acc;
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+        roots[q][wave][lane] = acc[q];
     __syncthreads();
     if (sub != 0)
         return;
-    const f32x4 *r = &roots[cb * S][lane];
-    f32x4 v;
-    if constexpr (S == 8)
-        v = ((r[0] + r[64]) + (r[128] + r[192])) + ((r[256] + r[320]) + (r[384] + r[448]));
-    else
-        v = (r[0] + r[64]) + (r[128] + r[192]);
     const int64_t col = col0 + (lane & 15);
     if (col >= N)
         return;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int64_t row = 4 * (lane >> 4) + rr;
-        if (row < M) {
-            if (out_bf16)
-                static_cast<uint16_t *>(out)[row * N + col] = f32_to_bf16_rne(v[rr]);
-            else
-                static_cast<float *>(out)[row * N + col] = v[rr];
+    for (int q = 0; q < RB; ++q) {
+        const f32x4 *r = &roots[q][cb * S][lane];
+        f32x4 v;
+        if constexpr (S == 8)
+            v = ((r[0] + r[64]) + (r[128] + r[192])) + ((r[256] + r[320]) + (r[384] + r[448]));
+        else
+            v = (r[0] + r[64]) + (r[128] + r[192]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t row = 16 * q + 4 * (lane >> 4) + rr;
+            if (row < M) {
+                if (out_bf16)
+                    static_cast<uint16_t *>(out)[row * N + col] = f32_to_bf16_rne(v[rr]);
+                else
+                    static_cast<float *>(out)[row * N + col] = v[rr];
+            }
         }
     }
 }
@@ -112,8 +124,12 @@ static hipError_t launch_rows(const uint16_t *A, const uint16_t *Wt, void *out, 
 {
     constexpr int BPW = 8 / S;
     const int64_t blocks = (N + 16 * BPW - 1) / (16 * BPW);
-    hipLaunchKernelGGL((gemm_rows_kernel<S, LWLOG, KS>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(512), 0, stream, A, Wt, out, out_bf16, M, N, K);
+    if (M <= 16)
+        hipLaunchKernelGGL((gemm_rows_kernel<S, LWLOG, KS, 1>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(512), 0, stream, A, Wt, out, out_bf16, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_rows_kernel<S, LWLOG, KS, 2>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(512), 0, stream, A, Wt, out, out_bf16, M, N, K);
     return hipGetLastError();
 }
 

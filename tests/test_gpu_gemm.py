@@ -154,7 +154,7 @@ def test_partition_combine_shapes(M, N):
                                    (4096, 16, 4096), (2048, 32, 130), (4096, 64, 96),
                                    (4096, 8, 256), (4096, 4, 256), (1024, 2, 200)])
 def test_few_rows_match_batch(K, L, N):
-    """One to 16 rows take the weight-streaming kernel (one workgroup per 16 output columns,
+    """One to 32 rows take the weight-streaming kernel (one workgroup per 16 output columns,
     eight subtrees of leaves per column block); the same rows inside a batch of 200 take the
     tile kernel.  Same bits, FP32 and bf16, ragged N; 4 leaves of 1024 and 2 leaves are shapes
     it leaves to the tile kernels."""
@@ -163,7 +163,7 @@ def test_few_rows_match_batch(K, L, N):
     note(f"few rows vs batch K={K} L={L} N={N}")
     big = u32(_run(A, Wt, L))
     bigb = _run(A, Wt, L, 1, iso.BF16)
-    for m in (1, 5, 16):
+    for m in (1, 5, 16, 17, 32):
         for start in (0, 150):
             assert np.array_equal(u32(_run(A[start:start + m], Wt, L)), big[start:start + m]), (m, start)
             assert np.array_equal(_run(A[start:start + m], Wt, L, 1, iso.BF16),
