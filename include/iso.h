@@ -339,7 +339,7 @@ iso_status iso_rmsnorm(const iso_contract *c, const void *x, const void *residua
  * r = k_i^T R, U <- U + (beta_i v_i) r, R <- alpha_i (R - (beta_i k_i) r);
  * P_c = R), not the stepped state.
  *
- * Contract: schedule ISO_SCHED_CPR_GDN, leaf_count = d (this build: 128),
+ * Contract: schedule ISO_SCHED_CPR_GDN, leaf_count = d (the kernels take 128),
  * leaf_size = C (1..64), vocab_chunk 0 (else ISO_ERR_CONTRACT; d != 128 is
  * ISO_ERR_SHAPE).  Layouts: q, k, v bf16 [T][H][d]; alpha, beta FP32
  * [T][H]; states FP32 [H][d][d] row-major; all 16-byte aligned.

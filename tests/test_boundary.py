@@ -320,3 +320,15 @@ def test_cpr_decode_rejections_before_launch():
     need = iso.cpr_workspace(c, 2, 16)
     assert _cpr_dec(c, wsb=need - 1) == 6
     assert _cpr_dec(c, ws=None) == 6
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says so, before any GPU work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
