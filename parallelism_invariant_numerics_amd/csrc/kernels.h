@@ -72,8 +72,7 @@ struct MoeBuffers {
     uint16_t *h;        // [T][k][I]
     float *e;           // [T][k][H]
     int32_t *counts;    // [E]
-    int32_t *offsets;   // [E + 1]
-    int32_t *rows;      // [T * k] (token * k + slot), grouped by expert, token order
+    int32_t *rows;      // [E][T]: expert e's entries (token * k + slot) in token order, counts[e] of them
     int32_t *tiles;     // [max_tiles][2]: (expert, first row within the expert)
     int32_t *ntiles;    // [1]
     int max_tiles;
