@@ -368,8 +368,9 @@ namespace {
 
 struct MoeFull {
     iso_moe_layout pub;
-    size_t counts, rows, tiles, ntiles;
+    size_t counts, rows, tiles, ntiles, blk;
     int max_tiles;
+    int nblk;  // 64-token blocks of the two-pass bucket (0: one pass per expert)
 };
 
 iso_status moe_dims(int64_t T, int64_t H, int64_t E, int64_t I, int top_k)
@@ -408,6 +409,10 @@ MoeFull moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int top_k)
     o += align_up((size_t)l.max_tiles * 2 * 4);
     l.ntiles = o;
     o += 256;
+    // per-block expert counts of the two-pass bucket (at most 16384 tokens)
+    l.nblk = T <= iso::kMoeBucketMaxT ? (int)((T + iso::kMoeBucketTok - 1) / iso::kMoeBucketTok) : 0;
+    l.blk = o;
+    o += align_up((size_t)l.nblk * (size_t)E * 4);
     l.pub.total = o;
     return l;
 }
@@ -622,6 +627,8 @@ iso_status iso_moe_combine(const iso_contract *gate_up, const iso_contract *down
     b.tiles = reinterpret_cast<int32_t *>(ws + l.tiles);
     b.ntiles = reinterpret_cast<int32_t *>(ws + l.ntiles);
     b.max_tiles = l.max_tiles;
+    b.blk_counts = l.nblk > 0 ? reinterpret_cast<int32_t *>(ws + l.blk) : nullptr;
+    b.nblk = l.nblk;
     return launch_status(iso::launch_moe(
         static_cast<const uint16_t *>(X), router_logits, static_cast<const uint16_t *>(Wg),
         static_cast<const uint16_t *>(Wu), static_cast<const uint16_t *>(Wd), Y, T, H, E, I,

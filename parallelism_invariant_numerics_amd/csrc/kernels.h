@@ -76,7 +76,13 @@ struct MoeBuffers {
     int32_t *tiles;     // [max_tiles][2]: (expert, first row within the expert)
     int32_t *ntiles;    // [1]
     int max_tiles;
+    int32_t *blk_counts;  // [nblk][E] per 64-token block (two-pass bucket), or null
+    int nblk;
 };
+
+// The two-pass bucket takes blocks of this many tokens, for T up to the limit.
+constexpr int kMoeBucketTok = 64;
+constexpr int64_t kMoeBucketMaxT = 16384;
 
 hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg,
                       const uint16_t *Wu, const uint16_t *Wd, float *Y, int64_t T, int64_t H,

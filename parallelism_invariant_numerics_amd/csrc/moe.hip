@@ -223,6 +223,87 @@ __global__ __launch_bounds__(256) void moe_bucket_kernel(const int32_t *idx, int
         counts[e] = count;
 }
 
+// Two-pass bucket (T <= kMoeBucketMaxT): the same lists, built from blocks of
+// 64 tokens.  A token's top_k experts are distinct, so in a block expert e
+// takes at most one entry per token, and an entry's place among the block's
+// entries of e is the number of earlier tokens of the block that chose e:
+// the population count of a 64-bit token mask below the token.  Counts and
+// masks are built with LDS atomics, whose results do not depend on their
+// order; entries land at the expert's count over the earlier blocks plus
+// that place, i.e. in token order.  Entries with an expert id outside
+// [0, E) (a token whose logits were all NaN) belong to no expert.
+__global__ __launch_bounds__(1024) void moe_bucket_count_kernel(const int32_t *idx, int32_t *blk,
+                                                                int64_t T, int E, int top_k)
+{
+    __shared__ int c_s[1024];
+    const int64_t b = blockIdx.x;
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        c_s[e] = 0;
+    __syncthreads();
+    const int64_t t0 = b * kMoeBucketTok;
+    const int nt = T - t0 < kMoeBucketTok ? static_cast<int>(T - t0) : kMoeBucketTok;
+    for (int j = threadIdx.x; j < nt * top_k; j += blockDim.x) {
+        const int e = idx[t0 * top_k + j];
+        if (e >= 0 && e < E)
+            atomicAdd(&c_s[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        blk[b * E + e] = c_s[e];
+}
+
+__global__ __launch_bounds__(1024) void moe_bucket_scatter_kernel(const int32_t *idx,
+                                                                  const int32_t *blk,
+                                                                  int32_t *rows, int32_t *counts,
+                                                                  int64_t T, int E, int top_k)
+{
+    __shared__ int base_s[1024];
+    __shared__ int part_s[1024];
+    __shared__ unsigned long long mask_s[1024];
+    const int64_t b = blockIdx.x;
+    const int64_t nb = gridDim.x;
+    // the expert's count over the earlier blocks: parts threads per expert
+    // each sum every parts-th block (integers: the order does not matter)
+    const int parts = static_cast<int>(blockDim.x) / E;
+    if (static_cast<int>(threadIdx.x) < parts * E) {
+        const int e = threadIdx.x % E, part = threadIdx.x / E;
+        int s = 0;
+#pragma unroll 4
+        for (int64_t q = part; q < b; q += parts)
+            s += blk[q * E + e];
+        part_s[part * E + e] = s;
+    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        mask_s[e] = 0ull;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int s = 0;
+        for (int part = 0; part < parts; ++part)
+            s += part_s[part * E + e];
+        base_s[e] = s;
+        if (b == nb - 1)
+            counts[e] = s + blk[b * E + e];
+    }
+    __syncthreads();
+    const int64_t t0 = b * kMoeBucketTok;
+    const int nt = T - t0 < kMoeBucketTok ? static_cast<int>(T - t0) : kMoeBucketTok;
+    for (int j = threadIdx.x; j < nt * top_k; j += blockDim.x) {
+        const int e = idx[t0 * top_k + j];
+        if (e >= 0 && e < E)
+            atomicOr(&mask_s[e], 1ull << (j / top_k));
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nt * top_k; j += blockDim.x) {
+        const int e = idx[t0 * top_k + j];
+        if (e >= 0 && e < E) {
+            const int tl = j / top_k;
+            const int place = __popcll(mask_s[e] & ((1ull << tl) - 1ull));
+            rows[static_cast<int64_t>(e) * T + base_s[e] + place] =
+                static_cast<int32_t>(t0 * top_k + j);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ plan
 
 // Work list of (expert, first row) tiles in expert order: thread e (E <=
@@ -617,8 +698,16 @@ hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    hipLaunchKernelGGL(moe_bucket_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream,
-                       b.idx, b.rows, b.counts, T * top_k, T);
+    if (b.nblk > 0) {
+        hipLaunchKernelGGL(moe_bucket_count_kernel, dim3(static_cast<unsigned>(b.nblk)), dim3(1024),
+                           0, stream, b.idx, b.blk_counts, T, (int)E, top_k);
+        hipLaunchKernelGGL(moe_bucket_scatter_kernel, dim3(static_cast<unsigned>(b.nblk)),
+                           dim3(1024), 0, stream, b.idx, b.blk_counts, b.rows, b.counts, T, (int)E,
+                           top_k);
+    } else {
+        hipLaunchKernelGGL(moe_bucket_kernel, dim3(static_cast<unsigned>(E)), dim3(256), 0, stream,
+                           b.idx, b.rows, b.counts, T * top_k, T);
+    }
     hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, stream, b.counts, b.tiles,
                        b.ntiles, (int)E);
     if ((err = hipGetLastError()) != hipSuccess)

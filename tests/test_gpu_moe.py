@@ -153,3 +153,24 @@ def test_moe_full_size():
     y1k, _ = _run(cfg["X"][:1024], cfg["logits"][:1024], cfg["Wg"], cfg["Wu"], cfg["Wd"], k, Lgu,
                   Ldn, dW)
     assert np.array_equal(y1k.view(np.uint32), y[:1024].view(np.uint32))
+
+
+def test_bucket_paths_agree():
+    """Up to 16384 tokens the per-expert lists are built from 64-token blocks (two passes);
+    above, one pass per expert over all entries.  A token's output bits are the same either
+    way: tokens of a 16500-token batch against the same tokens in batches of 1000 and 65."""
+    T, H, E, I, k = 16500, 64, 16, 64, 4
+    X = normal_bf16(31, (T, H), 1.0)
+    lg = normal_f32(32, (T, E))
+    Wg = normal_bf16(33, (E, I, H), 0.05)
+    Wu = normal_bf16(34, (E, I, H), 0.05)
+    Wd = normal_bf16(35, (E, H, I), 0.05)
+    dW = (dev(Wg), dev(Wu), dev(Wd))
+    note("moe bucket paths: 16500 tokens (one pass per expert)")
+    big, _ = _run(X, lg, Wg, Wu, Wd, k, 1, 1, dW)
+    rng = np.random.default_rng(36)
+    for n in (1000, 65):
+        sel = np.sort(rng.choice(T, n, replace=False))
+        note(f"moe bucket paths: {n} of them (64-token blocks)")
+        ys, _ = _run(X[sel], lg[sel], Wg, Wu, Wd, k, 1, 1, dW)
+        assert np.array_equal(ys.view(np.uint32), big[sel].view(np.uint32)), n
