@@ -27,14 +27,41 @@ namespace iso {
 
 // ------------------------------------------------------------------ route
 
-// Balanced tree over the 64 lanes of a wave in lane order (pairs (l, l^1),
-// then (l, l^2), ...); every lane ends with the root.
+// Balanced tree over the 64 lanes of a wave in lane order; every lane ends
+// with the root.  Inside each row of 16 lanes the levels pair lanes l ^ 1,
+// l ^ 2, then the other quad of the 8 and the other 8 of the 16 (DPP, the
+// same sums as l ^ 4 and l ^ 8 since IEEE addition is commutative), then
+// rows l ^ 16 and l ^ 32.
 __device__ __forceinline__ float wave_tree_sum(float v)
 {
-#pragma unroll
-    for (int mask = 1; mask < 64; mask <<= 1)
-        v = v + shfl_xor(v, mask);
-    return v;
+    v = row16_sum(v);
+    v = v + shfl_xor(v, 16);
+    return v + shfl_xor(v, 32);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, true);
+}
+
+// The wave's largest (value, -expert) pair: a total order, so any pairing of
+// lanes gives the same winner; DPP inside rows of 16, then l ^ 16 and l ^ 32.
+// NaN values never win.
+__device__ __forceinline__ void wave_argmax(float &bv, int &be)
+{
+    auto take = [&](float ov, int oe) {
+        if (ov > bv || (ov == bv && oe < be)) {
+            bv = ov;
+            be = oe;
+        }
+    };
+    take(dpp_mov<0xB1>(bv), dpp_int<0xB1>(be));
+    take(dpp_mov<0x4E>(bv), dpp_int<0x4E>(be));
+    take(dpp_mov<0x141>(bv), dpp_int<0x141>(be));
+    take(dpp_mov<0x140>(bv), dpp_int<0x140>(be));
+    take(shfl_xor(bv, 16), __shfl_xor(be, 16, 64));
+    take(shfl_xor(bv, 32), __shfl_xor(be, 32, 64));
 }
 
 // Balanced tree over n = 2^k register values in index order.
@@ -73,9 +100,9 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *logits, int
 #pragma unroll
     for (int q = 1; q < Q; ++q)
         mx = fmaxf(mx, lg[q]);
-#pragma unroll
-    for (int mask = 1; mask < 64; mask <<= 1)
-        mx = fmaxf(mx, shfl_xor(mx, mask));
+    mx = row16_max(mx);  // max is exact in any order
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
 
     float p[Q], blk[Q];
 #pragma unroll
@@ -104,15 +131,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float *logits, int
                 be = e;
             }
         }
-#pragma unroll
-        for (int mask = 1; mask < 64; mask <<= 1) {
-            const float ov = shfl_xor(bv, mask);
-            const int oe = __shfl_xor(be, mask, 64);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
+        wave_argmax(bv, be);
         // expert be sits in lane be & 63, register q = be >> 6 (the same on all lanes)
         float pv = 0.0f;
 #pragma unroll
