@@ -121,3 +121,13 @@ def cpr_pins():
         else:
             out[kind] = nums[0]
     return out
+
+
+def moe_combine_pins():
+    """Rows of moe_combine_pins.txt: top_k, gates [k], expert rows [k][H], y [H]."""
+    out = []
+    for k, gates, rows, y in _lines("moe_combine_pins.txt"):
+        e = [[float(v) for v in r.split()] for r in rows.split(";")]
+        out.append(dict(top_k=int(k), gates=[float(v) for v in gates.split()], e=e,
+                        y=[float(v) for v in y.split()]))
+    return out

@@ -4,6 +4,7 @@ import pytest
 from scipy.special import expit, softmax
 
 import oracle
+from pins import moe_combine_pins
 from iso_synth import bf16_bits_to_f32, f32_to_bf16_bits, normal_bf16, normal_f32
 
 
@@ -85,6 +86,53 @@ def test_integer_down_projection_exact():
     for t in range(T):
         for s in range(k):
             assert np.array_equal(e[t, s].astype(np.int64), wi[idx[t, s]] @ hi[t, s])
+
+
+def test_combine_pairing_pins():
+    # hand-worked outputs (tests/golden/moe_combine_pins.txt): distinct dyadic
+    # gates against unit-vector expert rows, so gate k must meet slot k's row
+    pins = moe_combine_pins()
+    assert len(pins) == 4
+    for p in pins:
+        k = p["top_k"]
+        gate = np.array([p["gates"]], dtype=np.float64)
+        e = np.array([p["e"]], dtype=np.float32)
+        assert gate.shape == (1, k) and e.shape[:2] == (1, k)
+        y = oracle.moe_combine(gate, e)
+        assert np.array_equal(y[0], np.array(p["y"])), (k, y[0], p["y"])
+        # several tokens at once: each token pairs its own gates and rows
+        g2 = np.concatenate([gate, gate[:, ::-1]])
+        e2 = np.concatenate([e, e])
+        y2 = oracle.moe_combine(g2, e2)
+        assert np.array_equal(y2[0], y[0])
+        assert np.array_equal(y2[1], (g2[1][:, None] * e2[1].astype(np.float64)).sum(0))
+
+
+def test_combine_distinct_experts_float64():
+    # the whole block with distinct experts: y is the gate-weighted sum of the
+    # expert outputs of the same slot (a float64 product-sum of the oracle's own
+    # gates and expert outputs; every term is exact in float64 up to one
+    # rounding per add)
+    X, lg, Wg, Wu, Wd = _small(T=12, E=16)
+    r = oracle.moe(X, lg, Wg, Wu, Wd, 4, 2, 2)
+    want = np.einsum("tk,tkh->th", r["gate"], r["e"].astype(np.float64))
+    assert np.allclose(r["y"], want, rtol=4 * 2.0 ** -52, atol=1e-300)
+    # the slots hold different experts, so a permuted pairing is far off
+    swapped = np.einsum("tk,tkh->th", r["gate"][:, ::-1], r["e"].astype(np.float64))
+    assert np.max(np.abs(swapped - r["y"])) > 1e-3
+
+
+def test_routing_order_closed_form():
+    # expert logits ln 3, ln 8, -30, ln 5: routing order (1, 3, 0) and gates
+    # 8/16, 5/16, 3/16 (the full softmax's denominator cancels in the
+    # renormalisation; exp(-30) only enters through it)
+    lg = np.log(np.array([[3.0, 8.0, np.exp(-30.0), 5.0]])).astype(np.float32)
+    lg[0, 2] = -30.0
+    idx, gate = oracle.moe_route(lg, 3)
+    assert idx.tolist() == [[1, 3, 0]]
+    p = np.exp(lg[0, [1, 3, 0]].astype(np.float64))
+    assert np.allclose(gate[0], p / p.sum(), rtol=1e-15, atol=0)
+    assert np.allclose(gate[0], [0.5, 0.3125, 0.1875], rtol=1e-6, atol=0)
 
 
 def test_token_permutation_equivariance():
