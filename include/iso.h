@@ -422,6 +422,23 @@ iso_status iso_moe_combine(const iso_contract *gate_up, const iso_contract *down
                            int64_t E, int64_t I, int top_k, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/*
+ * The expert FFN's activation on its own (the SwiGLU step of
+ * iso_moe_combine; [AGL] "Achieving Parallelism Invariance", EP bullet: the
+ * expert computations are part of the invariant region), for a dense FFN
+ * built from iso_gemm calls and for checking the MoE stage by stage:
+ *   h[i]   = bf16(silu(G[i]) * U[i]), rounded to nearest even;
+ *   act[i] = silu(G[i]) * U[i] in FP32 before that rounding (act may be NULL);
+ * silu(g) = g / (1 + e^-g), FP32, e^-g on the hardware exp2 of -g log2(e).
+ * It is the same device function as the MoE gate/up epilogue, so G and U
+ * with the bits of that stage (iso_gemm with the gate_up contract gives
+ * them) reproduce its h bit for bit.  G, U, act: FP32 [n]; h: bf16 [n];
+ * device memory, no alignment needed; act and h must not overlap G or U.
+ * n == 0 returns ISO_OK; n < 0 or a NULL G, U or h gives ISO_ERR_ARG.
+ */
+iso_status iso_swiglu(const float *G, const float *U, float *act, void *h, int64_t n,
+                      void *stream);
+
 /* Static description of a status code. */
 const char *iso_status_str(iso_status s);
 

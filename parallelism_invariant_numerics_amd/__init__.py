@@ -24,7 +24,7 @@ import torch  # noqa: F401  (load order matters)
 __all__ = [
     "IsoError", "Contract", "contract", "digest", "check_identity", "check_partitions",
     "gemm_workspace", "gemm", "gemm_baseline", "lmhead_workspace", "lmhead_logprob",
-    "moe_workspace", "moe_layout", "moe_combine", "moe_stages",
+    "moe_workspace", "moe_layout", "moe_combine", "moe_stages", "swiglu",
     "cpr_contract", "cpr_workspace", "cpr_prefill", "cpr_decode_step",
     "lib", "LIB_PATH", "F32", "BF16", "VOCAB_CHUNK", "version",
 ]
@@ -117,6 +117,7 @@ _SIGS = {
                            ctypes.c_char_p], _I),
     "iso_table_check": ([ctypes.POINTER(Composition), ctypes.c_size_t, ctypes.c_char_p,
                          ctypes.c_char_p, _CP, _I], _I),
+    "iso_swiglu": ([_P, _P, _P, _P, _I64, _P], _I),
     "iso_status_str": ([_I], ctypes.c_char_p),
     "iso_version": ([], ctypes.c_char_p),
     "iso_last_launch_error": ([], ctypes.c_char_p),
@@ -470,6 +471,23 @@ def moe_combine(X, router_logits, Wg, Wu, Wd, top_k: int, gate_up: Contract, dow
                             None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
         "iso_moe_combine")
     return out
+
+
+def swiglu(G, U, *, act=True, stream=None):
+    """h = bf16(silu(G) * U) element by element (G, U float32 device tensors
+    of one shape), with the MoE gate/up stage's device function.  Returns h
+    (bfloat16), or (act, h) with the FP32 activation before rounding when
+    act is True."""
+    torch = _torch()
+    if tuple(G.shape) != tuple(U.shape):
+        raise ValueError("G and U must have one shape")
+    gp = _dev_ptr(G, "G", torch.float32)
+    up = _dev_ptr(U, "U", torch.float32)
+    h = torch.empty(G.shape, dtype=torch.bfloat16, device=G.device)
+    a = torch.empty(G.shape, dtype=torch.float32, device=G.device) if act else None
+    _ok(lib.iso_swiglu(gp, up, None if a is None else a.data_ptr(), h.data_ptr(), G.numel(),
+                       _stream(stream)), "iso_swiglu")
+    return (a, h) if act else h
 
 
 def moe_stages(workspace, T: int, H: int, E: int, I: int, top_k: int) -> dict:

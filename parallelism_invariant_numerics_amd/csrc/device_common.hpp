@@ -58,6 +58,17 @@ __device__ __forceinline__ float exp_neg(float x)
     return __builtin_amdgcn_exp2f(x * kLog2e);
 }
 
+// SwiGLU activation of one element, silu(g) * u with silu(g) = g / (1 + e^-g)
+// (e^-g on the hardware exp2, as in exp_neg); FP32, no contraction.  The MoE
+// gate/up epilogue and iso_swiglu share it, so the same (g, u) bits give the
+// same activation bits in both.
+__device__ __forceinline__ float swiglu_act(float g, float u)
+{
+    const float kLog2e = 1.44269504088896340736f;
+    const float ex = __builtin_amdgcn_exp2f(-g * kLog2e);
+    return (g / (1.0f + ex)) * u;
+}
+
 // Natural log for the final logprob (one call per row): ROCm's logf.
 __device__ __forceinline__ float log_f32(float x) { return logf(x); }
 

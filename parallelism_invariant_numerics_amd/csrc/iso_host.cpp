@@ -636,6 +636,20 @@ iso_status iso_moe_combine(const iso_contract *gate_up, const iso_contract *down
         (int)down->leaf_size, b, static_cast<hipStream_t>(stream)));
 }
 
+iso_status iso_swiglu(const float *G, const float *U, float *act, void *h, int64_t n,
+                      void *stream)
+{
+    if (n < 0)
+        return ISO_ERR_ARG;
+    if (n == 0)
+        return ISO_OK;
+    if (!G || !U || !h)
+        return ISO_ERR_ARG;
+    clear_stale_error();
+    return launch_status(iso::launch_swiglu(G, U, act, static_cast<uint16_t *>(h), n,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 const char *iso_status_str(iso_status s)
 {
     switch (s) {

@@ -89,4 +89,8 @@ hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg
                       int64_t E, int64_t I, int top_k, int gu_leaves, int gu_leaf_size,
                       int dn_leaves, int dn_leaf_size, const MoeBuffers &b, hipStream_t stream);
 
+// h[i] = bf16(silu(G[i]) U[i]), act[i] (when not null) the FP32 value.
+hipError_t launch_swiglu(const float *G, const float *U, float *act, uint16_t *h, int64_t n,
+                         hipStream_t stream);
+
 }  // namespace iso

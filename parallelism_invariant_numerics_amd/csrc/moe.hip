@@ -496,7 +496,6 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs &a, const MoeTask
         lds_barrier();
         if constexpr (GATE_UP) {
             constexpr int UPT = 64 * (kGuCols / 8) / C::kThreads;  // units per thread
-            const float kLog2e = 1.44269504088896340736f;
             uint16_t *o = static_cast<uint16_t *>(a.out) + t.n0;
             const bool al = (reinterpret_cast<uintptr_t>(o) % 16 == 0) && (a.N % 8 == 0);
             const int cmax = a.N - t.n0 < kGuCols ? static_cast<int>(a.N - t.n0) : kGuCols;
@@ -533,11 +532,8 @@ __device__ __forceinline__ void moe_epilogue(const MoeGemmArgs &a, const MoeTask
                                      u1[k][0], u1[k][1], u1[k][2], u1[k][3]};
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float ex = __builtin_amdgcn_exp2f(-gs[e] * kLog2e);
-                    const float sg = gs[e] / (1.0f + ex);
-                    v[e] = sg * us[e];
-                }
+                for (int e = 0; e < 8; ++e)
+                    v[e] = swiglu_act(gs[e], us[e]);
                 store8_bf16(o + static_cast<int64_t>(dst[k]) * a.N + 8 * q, v,
                             al && 8 * q + 8 <= cmax, cmax - 8 * q);
             }
@@ -769,6 +765,34 @@ hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg
     if (blocks > 0)
         hipLaunchKernelGGL(moe_combine_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                            stream, b.gate, b.e, Y, T, H, top_k);
+    return hipGetLastError();
+}
+
+// h[i] = bf16(silu(G[i]) U[i]) and, when act is given, act[i] = the FP32
+// value before the rounding: the expert FFN's activation on its own, with
+// the device function of the gate/up epilogue.
+__global__ __launch_bounds__(256) void swiglu_kernel(const float *G, const float *U, float *act,
+                                                     uint16_t *h, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += stride) {
+        const float v = swiglu_act(G[i], U[i]);
+        if (act)
+            act[i] = v;
+        h[i] = f32_to_bf16_rne(v);
+    }
+}
+
+hipError_t launch_swiglu(const float *G, const float *U, float *act, uint16_t *h, int64_t n,
+                         hipStream_t stream)
+{
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192)
+        blocks = 8192;
+    if (blocks > 0)
+        hipLaunchKernelGGL(swiglu_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                           stream, G, U, act, h, n);
     return hipGetLastError();
 }
 

@@ -332,3 +332,13 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+
+
+def test_swiglu_rejections_before_launch():
+    f = iso.lib.iso_swiglu
+    assert f(FAKE, FAKE, None, FAKE, 0, None) == 0       # empty: nothing launched
+    assert f(FAKE, FAKE, None, FAKE, -1, None) == 1      # negative size
+    assert f(None, FAKE, None, FAKE, 8, None) == 1
+    assert f(FAKE, None, FAKE, FAKE, 8, None) == 1
+    assert f(FAKE, FAKE, FAKE, None, 8, None) == 1
+

@@ -90,6 +90,43 @@ def test_run_to_run_determinism():
     assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
 
 
+def test_bits_across_streams_and_launch_order():
+    # the same GEMM enqueued on two streams (default priority) that run at
+    # the same time, each behind other work, in both launch orders, and with
+    # its partitions' roots on a third: every result has the bits of a lone
+    # call on the current stream (no float atomics, no order from timing)
+    t = torch()
+    A = normal_bf16(17, (1100, 2048), 1.0)
+    Wt = normal_bf16(18, (700, 2048), 0.02)
+    A2 = normal_bf16(19, (3000, 2048), 1.0)
+    c = iso.contract(8, 256, 0)
+    dA, dW, dA2 = dev(A), dev(Wt), dev(A2)
+    note("streams: reference call")
+    ref = u32(host(iso.gemm(dA, dW, c)))
+    t.cuda.synchronize()
+    s1, s2, s3 = t.cuda.Stream(), t.cuda.Stream(), t.cuda.Stream()
+    outs = []
+    for order in range(2):
+        note(f"streams: concurrent calls, order {order}")
+        o = [t.empty((1100, 700), dtype=t.float32, device="cuda") for _ in range(3)]
+        f = [t.empty((3000, 700), dtype=t.float32, device="cuda") for _ in range(2)]
+        ws = t.empty(iso.gemm_workspace(c, 1100, 700, 4), dtype=t.uint8, device="cuda")
+        t.cuda.synchronize()
+        first, second = (s1, s2) if order == 0 else (s2, s1)
+        with t.cuda.stream(first):
+            iso.gemm(dA2, dW, c, out=f[0])       # other work ahead of the call
+            iso.gemm(dA, dW, c, out=o[0])
+        with t.cuda.stream(second):
+            iso.gemm(dA, dW, c, out=o[1])
+            iso.gemm(dA2, dW, c, out=f[1])
+        with t.cuda.stream(s3):
+            iso.gemm(dA, dW, c, out=o[2], partitions=4, workspace=ws)
+        t.cuda.synchronize()
+        outs += [u32(host(x)) for x in o]
+    for i, x in enumerate(outs):
+        assert np.array_equal(x, ref), i
+
+
 def test_empty_problem():
     c = iso.contract(4, 64, 0)
     t = torch()

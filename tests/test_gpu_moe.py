@@ -3,19 +3,25 @@ bit-identity of every token's output across token orderings.
 
 Stages (the workspace keeps each stage's output):
   route    expert ids equal the oracle's exactly; gates within 4e-7 relative;
-  gate/up  bf16 h equals the oracle's activation rounded to bf16, or differs
-           by one bf16 step where the activation lies within its tolerance of
-           a rounding midpoint (the decision is taken in FP32 on both sides,
-           from G and U that agree to 1e-5 * sum|x w|);
-  down     e = h Wd with the GPU's own h, within 1e-5 * sum|h w|;
-  combine  y within 1e-5 * sum_k |g_k e_k| of the oracle's combine of the
+  gate/up  G and U of each expert's rows from iso_gemm with the gate/up
+           contract (the same leaves and tree, so the bits of the MoE stage)
+           are within 1e-5 * sum|x w| of the oracle; the MoE's bf16 h equals,
+           bit for bit, bf16 of the GPU's own FP32 activation (iso_swiglu, the
+           epilogue's device function, on those G and U); that activation is
+           within the propagated tolerance of the oracle's;
+  down     e equals iso_gemm(h, Wd[e]) with the down contract bit for bit, and
+           is within 1e-5 * sum|h w| of the oracle's down projection of the
+           GPU's own h;
+  combine  y equals the FP32 left fold, in routing order, of the GPU's own
+           gates and e with each product rounded before its add, bit for bit,
+           and is within 1e-5 * sum_k |g_k e_k| of the oracle's combine of the
            GPU's e with the oracle's gates.
 """
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import dev, host, note, torch
+from gpu_util import absdot, check_gemm_tol, dev, host, note, torch
 from iso_synth import bf16_bits_to_f32, make_config, normal_bf16, normal_f32
 
 pytestmark = pytest.mark.gpu
@@ -37,40 +43,59 @@ def _run(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, dW=None):
     return host(y), {n: host(v) for n, v in st.items()}
 
 
+def fold32(gate, e):
+    """FP32 left fold over the slots: y = g0 e0, then y = y + g_k e_k, each
+    product rounded to FP32 before its add (numpy float32 never fuses)."""
+    g = np.asarray(gate, dtype=np.float32)
+    e = np.asarray(e, dtype=np.float32)
+    y = g[:, 0, None] * e[:, 0]
+    for s in range(1, g.shape[1]):
+        y = y + g[:, s, None] * e[:, s]
+    return y
+
+
 def _check_stages(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, y, st, what):
     T, H = X.shape
     E, I, _ = Wg.shape
     idx, gate = oracle.moe_route(lg, k)
     assert np.array_equal(st["idx"], idx), what
     assert np.allclose(st["gate"], gate, rtol=4e-7, atol=0), what
-    # gate/up: oracle G, U per expert on the GPU's routing
-    x = bf16_bits_to_f32(X).astype(np.float64)
-    act = np.zeros((T, k, I))
-    tol = np.zeros((T, k, I))
+    cg = iso.contract(Lgu, H // Lgu, 0)
+    cd = iso.contract(Ldn, I // Ldn, 0)
+    act_or, _ = oracle.moe_gate_up(X, Wg, Wu, idx, Lgu)
     for e in np.unique(idx):
         tt, ss = np.nonzero(idx == e)
-        G = oracle.gemm(X[tt], Wg[e], Lgu).astype(np.float64)
-        U = oracle.gemm(X[tt], Wu[e], Lgu).astype(np.float64)
-        adg = np.abs(x[tt]) @ np.abs(bf16_bits_to_f32(Wg[e]).astype(np.float64)).T
-        adu = np.abs(x[tt]) @ np.abs(bf16_bits_to_f32(Wu[e]).astype(np.float64)).T
-        sig = 1.0 / (1.0 + np.exp(-G))
-        silu = G * sig
-        dsilu = np.abs(sig * (1.0 + G * (1.0 - sig)))
-        act[tt, ss] = silu * U
-        tol[tt, ss] = (dsilu * np.abs(U) * 1e-5 * adg + np.abs(silu) * 1e-5 * adu
-                       + 8 * 2.0 ** -24 * np.abs(silu * U))
-    h = bf16_bits_to_f32(st["h"]).astype(np.float64)
-    half_ulp = np.abs(act) * 2.0 ** -8 + 1e-30  # one bf16 rounding step, bounds the half-ulp too
-    assert np.all(np.abs(h - act) <= half_ulp + tol), what
-    # down with the GPU's own h
-    e_or = oracle.moe_down(st["h"], Wd, st["idx"], Ldn).astype(np.float64)
-    hh = np.abs(h)
-    for slot in range(k):
-        for tt in range(T):
-            ad = hh[tt, slot] @ np.abs(bf16_bits_to_f32(Wd[st["idx"][tt, slot]]).astype(np.float64)).T
-            err = np.abs(st["e"][tt, slot] - e_or[tt, slot])
-            assert np.all(err <= 1e-5 * ad), (what, tt, slot)
-    # combine with the oracle's gates and the GPU's e
+        # gate/up: the plain GEMM entry point gives the MoE stage's G and U bits
+        dX = dev(X[tt])
+        G = iso.gemm(dX, dev(Wg[e]), cg)
+        U = iso.gemm(dX, dev(Wu[e]), cg)
+        act, h = iso.swiglu(G, U)
+        assert np.array_equal(st["h"][tt, ss], host(h)), (what, "h", e)
+        Gh, Uh = host(G).astype(np.float64), host(U).astype(np.float64)
+        G_or = oracle.gemm(X[tt], Wg[e], Lgu).astype(np.float64)
+        U_or = oracle.gemm(X[tt], Wu[e], Lgu).astype(np.float64)
+        adg, adu = absdot(X[tt], Wg[e]), absdot(X[tt], Wu[e])
+        check_gemm_tol(Gh, G_or, adg, f"{what} G e={e}")
+        check_gemm_tol(Uh, U_or, adu, f"{what} U e={e}")
+        # the FP32 activation: G, U tolerances through silu(G) U, plus the
+        # roundings of both sides (the GPU's exp2 of a rounded -G log2 e adds
+        # |G| 2^-24 relative)
+        sig = 1.0 / (1.0 + np.exp(-G_or))
+        silu = G_or * sig
+        dsilu = np.abs(sig * (1.0 + G_or * (1.0 - sig)))
+        tol = (dsilu * np.abs(U_or) * 1e-5 * adg + np.abs(silu) * 1e-5 * adu
+               + np.abs(silu * U_or) * 2.0 ** -24 * (10.0 + np.abs(G_or)))
+        err = np.abs(host(act).astype(np.float64) - act_or[tt, ss].astype(np.float64))
+        assert np.all(err <= tol), (what, "act", e, float(np.max(err / np.maximum(tol, 1e-300))))
+        # down: the plain GEMM of the MoE's own h gives its e bit for bit
+        hrows = st["h"][tt, ss]
+        eg = host(iso.gemm(dev(hrows), dev(Wd[e]), cd))
+        assert np.array_equal(eg.view(np.uint32), st["e"][tt, ss].view(np.uint32)), (what, "e", e)
+        e_or = oracle.gemm(hrows, Wd[e], Ldn)
+        check_gemm_tol(st["e"][tt, ss], e_or, absdot(hrows, Wd[e]), f"{what} e e={e}")
+    # combine: the FP32 fold of the GPU's own gates and e, bit for bit
+    assert np.array_equal(y.view(np.uint32), fold32(st["gate"], st["e"]).view(np.uint32)), what
+    # and the oracle's combine with the oracle's gates and the GPU's e
     y_or = oracle.moe_combine(gate, st["e"])
     scale = np.einsum("tk,tkh->th", np.abs(gate), np.abs(st["e"].astype(np.float64)))
     assert np.all(np.abs(y - y_or) <= 1e-5 * scale + 1e-30), what
