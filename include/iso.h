@@ -268,6 +268,25 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
                               size_t workspace_bytes, void *stream);
 
 /*
+ * iso_lmhead_logprob for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same numbers, bit for bit, with the workspace taken from
+ * a static device array of ISO_LMHEAD_NOALLOC_BYTES that the library holds
+ * on every GPU it runs on until the process ends.  The call allocates and
+ * frees nothing; the first call on a device looks up that device's copy.
+ * One partition (arguments as iso_lmhead_logprob without partitions and
+ * workspace).  A shape whose statistics (M * ceil(V / 128) * 8 bytes plus
+ * M * 4, each rounded up to 256) exceed the scratch gives ISO_ERR_WORKSPACE
+ * before any launch: at V = 151936 up to 3532 rows fit.  Every call on one
+ * GPU shares the one scratch: calls that overlap on a GPU (two streams, two
+ * threads) race and must be ordered by the caller.
+ */
+#define ISO_LMHEAD_NOALLOC_BYTES ((size_t)32 << 20)
+iso_status iso_lmhead_logprob_noalloc(const iso_contract *c, const void *H, const void *Wvt,
+                                      const int32_t *tok, float *logprob, int64_t M, int64_t V,
+                                      int64_t K, void *stream);
+
+/*
  * The vocabulary-sharded LM-head, split at its exchange point (one GPU
  * stands in for the ranks of a vocabulary-parallel layer; [AGL] "Achieving
  * Parallelism Invariance": partials are combined by the fixed tree whatever

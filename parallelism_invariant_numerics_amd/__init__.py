@@ -24,6 +24,7 @@ import torch  # noqa: F401  (load order matters)
 __all__ = [
     "IsoError", "Contract", "contract", "digest", "check_identity", "check_partitions",
     "gemm_workspace", "gemm", "gemm_baseline", "lmhead_workspace", "lmhead_logprob",
+    "lmhead_logprob_noalloc", "LMHEAD_NOALLOC_BYTES",
     "moe_workspace", "moe_layout", "moe_combine", "moe_stages", "swiglu",
     "cpr_contract", "cpr_workspace", "cpr_prefill", "cpr_decode_step",
     "lib", "LIB_PATH", "F32", "BF16", "VOCAB_CHUNK", "version",
@@ -98,6 +99,7 @@ _SIGS = {
     "iso_lmhead_workspace": ([_CP, _I64, _I64, _I], ctypes.c_size_t),
     "iso_lmhead_logprob": ([_CP, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P],
                            _I),
+    "iso_lmhead_logprob_noalloc": ([_CP, _P, _P, _P, _P, _I64, _I64, _I64, _P], _I),
     "iso_moe_layout_of": ([_I64, _I64, _I64, _I64, _I, _P], _I),
     "iso_moe_workspace": ([_I64, _I64, _I64, _I64, _I], ctypes.c_size_t),
     "iso_moe_combine": ([_CP, _CP, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _P,
@@ -284,6 +286,29 @@ def lmhead_logprob(H, Wvt, tok, c: Contract, *, out=None, partitions: int = 1,
                                _dev_ptr(out, "out", torch.float32), M, V, K, partitions,
                                None if ws is None else ws.data_ptr(), wsb, _stream(stream)),
         "iso_lmhead_logprob")
+    return out
+
+
+LMHEAD_NOALLOC_BYTES = 32 << 20  # ISO_LMHEAD_NOALLOC_BYTES
+
+
+def lmhead_logprob_noalloc(H, Wvt, tok, c: Contract, *, out=None, stream=None):
+    """lmhead_logprob (one partition) with the library's static device
+    scratch as the workspace: the library call allocates nothing (``out`` is
+    allocated here when not given).  Calls that overlap on one GPU race."""
+    torch = _torch()
+    M, K = H.shape
+    V = Wvt.shape[0]
+    if Wvt.dim() != 2 or Wvt.shape[1] != K:
+        raise ValueError("Wvt must be [V][K]")
+    if tok.shape != (M,):
+        raise ValueError("tok must be [M]")
+    if out is None:
+        out = torch.empty(M, dtype=torch.float32, device=H.device)
+    _ok(lib.iso_lmhead_logprob_noalloc(ctypes.byref(c), _bf16_ptr(H, "H"), _bf16_ptr(Wvt, "Wvt"),
+                                       _dev_ptr(tok, "tok", torch.int32),
+                                       _dev_ptr(out, "out", torch.float32), M, V, K,
+                                       _stream(stream)), "iso_lmhead_logprob_noalloc")
     return out
 
 

@@ -319,6 +319,45 @@ iso_status iso_lmhead_logprob(const iso_contract *c, const void *H, const void *
     return launch_status(iso::launch_lmhead_finish(stats, target, tok, logprob, M, V, st));
 }
 
+iso_status iso_lmhead_logprob_noalloc(const iso_contract *c, const void *H, const void *Wvt,
+                                      const int32_t *tok, float *logprob, int64_t M, int64_t V,
+                                      int64_t K, void *stream)
+{
+    static_assert(iso::kLmNoallocBytes == ISO_LMHEAD_NOALLOC_BYTES, "one scratch size");
+    iso_status s = check_contract(c, ISO_VOCAB_CHUNK);
+    if (s != ISO_OK)
+        return s;
+    if ((s = check_gemm_shape(c, M, V, K)) != ISO_OK)
+        return s;
+    if (V < 1 || V > kMaxVocab)
+        return ISO_ERR_SHAPE;
+    if (M == 0)
+        return ISO_OK;
+    if (!H || !Wvt || !tok || !logprob || !aligned16(H) || !aligned16(Wvt))
+        return ISO_ERR_ARG;
+    const int parts = internal_parts(c, 1);
+    const LmLayout l = lm_layout(M, V, parts);
+    if (l.total > ISO_LMHEAD_NOALLOC_BYTES)
+        return ISO_ERR_WORKSPACE;
+
+    clear_stale_error();
+    void *scratch = nullptr;
+    const hipError_t se = iso::lmhead_noalloc_scratch(&scratch);
+    if (se != hipSuccess)
+        return launch_status(se);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(scratch);
+    float *stats = reinterpret_cast<float *>(ws + l.stats);
+    float *target = reinterpret_cast<float *>(ws + l.target);
+    float *roots = parts > 1 ? reinterpret_cast<float *>(ws + l.roots) : nullptr;
+    hipError_t e = iso::launch_lmhead_stats(
+        static_cast<const uint16_t *>(H), static_cast<const uint16_t *>(Wvt), tok, stats, target,
+        roots, M, V, K, (int)c->leaf_count / parts, (int)c->leaf_size, parts, 0, V, st);
+    if (e != hipSuccess)
+        return launch_status(e);
+    return launch_status(iso::launch_lmhead_finish(stats, target, tok, logprob, M, V, st));
+}
+
 iso_status iso_lmhead_shard_stats(const iso_contract *c, const void *H, const void *Wvt_shard,
                                   const int32_t *tok, float *stats, float *target, int64_t M,
                                   int64_t V, int64_t v_begin, int64_t v_end, int64_t K,

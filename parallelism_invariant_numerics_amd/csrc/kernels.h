@@ -89,6 +89,15 @@ hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg
                       int64_t E, int64_t I, int top_k, int gu_leaves, int gu_leaf_size,
                       int dn_leaves, int dn_leaf_size, const MoeBuffers &b, hipStream_t stream);
 
+// Bytes of the LM-head's static device scratch (lmhead.hip), the workspace
+// of iso_lmhead_logprob_noalloc; equals ISO_LMHEAD_NOALLOC_BYTES.
+constexpr size_t kLmNoallocBytes = (size_t)32 << 20;
+
+// Device address of that scratch on the current device, looked up with
+// hipGetSymbolAddress on the first call per device and kept; the error of
+// the lookup otherwise.
+hipError_t lmhead_noalloc_scratch(void **ptr);
+
 // h[i] = bf16(silu(G[i]) U[i]), act[i] (when not null) the FP32 value.
 hipError_t launch_swiglu(const float *G, const float *U, float *act, uint16_t *h, int64_t n,
                          hipStream_t stream);

@@ -20,6 +20,8 @@
 // The logits never leave registers on the fused path (one partition).  With
 // several partitions the partition roots of the logits go through the
 // workspace and the same epilogue function runs on their folded values.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_core.hpp"
@@ -630,6 +632,44 @@ hipError_t launch_lmhead_stats(const uint16_t *H, const uint16_t *Wvt, const int
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// The workspace of iso_lmhead_logprob_noalloc: chunk statistics and target
+// logits of one call, for callers that cannot allocate.  Every GPU the
+// library runs on holds its own copy until the process ends; calls that
+// overlap on one GPU share it and race.  Nothing in it needs clearing: a
+// call writes every chunk pair of its rows before the finish kernel reads
+// them, and reads a target logit only for a token id it has written.
+static __device__ __align__(256) char scratch[kLmNoallocBytes];
+
+hipError_t lmhead_noalloc_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void *> addr[kMaxDevices];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            // with `dev` current: each GPU's copy has its own address; the
+            // name `scratch` itself is a host-side stand-in, never passed on
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            if (!p)
+                return hipErrorInvalidSymbol;
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_lmhead_finish(const float *ws_stats, const float *ws_target,

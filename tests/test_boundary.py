@@ -342,3 +342,17 @@ def test_swiglu_rejections_before_launch():
     assert f(FAKE, None, FAKE, FAKE, 8, None) == 1
     assert f(FAKE, FAKE, FAKE, None, 8, None) == 1
 
+
+def test_lmhead_noalloc_rejections_before_launch():
+    f = iso.lib.iso_lmhead_logprob_noalloc
+    c = iso.contract(8, 256, 128)
+    cr = ctypes.byref(c)
+    # the statistics of 3533 rows of a 151936-id vocabulary exceed the scratch
+    assert f(cr, FAKE, FAKE, FAKE, FAKE, 3533, 151936, 2048, None) == 6
+    assert f(cr, FAKE, FAKE, FAKE, FAKE, 10, 151936, 1024, None) == 2   # K != L * m
+    assert f(cr, None, FAKE, FAKE, FAKE, 10, 151936, 2048, None) == 1
+    assert f(cr, FAKE + 2, FAKE, FAKE, FAKE, 10, 151936, 2048, None) == 1  # unaligned
+    assert f(cr, FAKE, FAKE, FAKE, FAKE, 0, 151936, 2048, None) == 0    # empty
+    assert f(ctypes.byref(iso.contract(8, 256, 0)), FAKE, FAKE, FAKE, FAKE, 10, 1000, 2048,
+             None) == 8                                                   # no vocab chunk
+    assert iso.LMHEAD_NOALLOC_BYTES == 32 << 20
