@@ -6,15 +6,28 @@ One step is one invariant GEMM of the prefill-shaped linear layer
 (A [4096 x 2048] bf16 times W [2048 x 2048] bf16, 8 contiguous leaves of 256
 along K, FP32 accumulation and fixed tree, bf16 output) with its inputs
 resident in HBM; ``value`` is TFLOP/s (2 M N K per step).  The same run also
-times, as sub-measurements reported in the JSON line: the non-invariant
-comparison kernel and torch's linear layer on the same shape, the
-invariance-sweep shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8
-partitions, the LM-head logprob workload (8192 rows x 2048 x 151936
-vocabulary) in rows/s, the MoE FFN block (4096 tokens, 128 experts, top-8),
-the RMSNorm with residual add in front of the LM-head (8192 x 2048, GB/s),
-the CPR gated delta rule (16 heads of 128, 4096 tokens, chunk 64: prefill
-ms and decode us per token), plus bitwise invariance checks (CPR: decode of
-the last chunk equals the prefill).  Prints ONE JSON line.
+times, as sub-measurements reported in the JSON line:
+  * the cost of invariance next to a non-invariant comparator on every
+    workload: the same tiles with one accumulator over all of K and torch's
+    linear layer (prefill and 4096^3 sweep shapes), the fused LM-head with one
+    accumulator per logit and torch's linear + log_softmax + gather, the MoE
+    block with one-leaf contracts and a plain torch expert loop scattering
+    with index_add_;
+  * the sweep shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8 partitions and
+    at batches of 1, 8 and 64 rows; the LM-head logprob workload (8192 rows x
+    2048 x 151936 vocabulary) in rows/s, fused, over 8 vocabulary shards and
+    one row per call; the MoE FFN block (4096 tokens, 128 experts, top-8); the
+    RMSNorm with residual add in front of the LM-head (8192 x 2048, GB/s); the
+    CPR gated delta rule (16 heads of 128, 4096 tokens, chunk 64);
+  * bitwise invariance checks (rows alone against the batch, partitions,
+    vocabulary shards, token orderings, decode against prefill);
+  * workspace bytes of each entry point at these shapes.
+With the CPU baseline (default) the oracle is timed on the host cores: the
+prefill GEMM on all threads (``cpu_baseline``) and on one thread, the tiny
+workload, 64 LM-head rows over the full vocabulary, the 4096^3 sweep layer and
+the MoE block; and |gpu - oracle| percentiles with the largest error over
+tolerance are reported for 4096 sampled prefill elements and those 64 rows.
+Prints ONE JSON line.
 
 Inputs are seeded synthetic data with the workloads' shapes and
 distributions (no dataset or trained weights are involved).
@@ -126,21 +139,24 @@ def _traffic(kernel_hash):
     return rec.get("bytes_per_launch")
 
 
-def _cpu_baseline(cfg, target_s=10.0):
+def _timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def _cpu_baseline(cfg, target_s=6.0):
     """The oracle (untuned) on the same GEMM: a row sample sized from a 256-row calibration run
     (the whole job at most), repeated until about target_s of CPU time have passed."""
     import oracle
     A, Wt, L = cfg["A"], cfg["Wt"], cfg["leaves"]
     rows = 256
-    t0 = time.perf_counter()
-    oracle.gemm(A[:rows], Wt, L)
-    dt = time.perf_counter() - t0
+    _, dt = _timed(lambda: oracle.gemm(A[:rows], Wt, L))
     rows = int(min(cfg["M"], max(16, rows * target_s / max(dt, 1e-6))))
     reps, total = 0, 0.0
     while reps == 0 or (total < target_s and reps < 100):
-        t0 = time.perf_counter()
-        oracle.gemm(A[:rows], Wt, L)
-        total += time.perf_counter() - t0
+        _, dt = _timed(lambda: oracle.gemm(A[:rows], Wt, L))
+        total += dt
         reps += 1
     flops = 2.0 * rows * cfg["N"] * cfg["K"] * reps
     what = (f"the whole prefill GEMM ({rows}x{cfg['N']}x{cfg['K']}, 8 leaves)" if rows == cfg["M"]
@@ -148,6 +164,73 @@ def _cpu_baseline(cfg, target_s=10.0):
     what += f", {reps} run{'s' if reps > 1 else ''}"
     return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle", "sample": f"{what}, {total:.1f} s"}
+
+
+def _cpu_more(cfg, lm, mc, single_s=3.0):
+    """Oracle timings of the other workloads on all host threads (the tiny one
+    whole, 64 rows of the LM-head over the full vocabulary, the 4096^3 sweep
+    layer at one partition, the MoE block whole) and of a prefill-GEMM row
+    sample on one thread."""
+    import oracle
+    from iso_synth import make_config, normal_bf16
+    out = {}
+    ti = make_config("tiny")
+    _, dt = _timed(lambda: (oracle.gemm(ti["A"], ti["Wt"], ti["leaves"]),
+                            oracle.lmhead_logprob(ti["A"], ti["Wt"], ti["tok"], ti["leaves"])))
+    out["tiny_gemm_logprob_s"] = round(dt, 4)
+    rows = np.sort(np.random.default_rng(2025).choice(lm["M"], 64, replace=False))
+    (lp, _, _), dt = _timed(lambda: oracle.lmhead_logprob(lm["H"][rows], lm["Wvt"], lm["tok"][rows],
+                                                          lm["leaves"]))
+    out["lmhead_64rows_s"] = round(dt, 3)
+    out["lmhead_rows_per_s"] = round(64 / dt, 2)
+    Ws = normal_bf16(401, (4096, 4096), 0.02)
+    As = normal_bf16(403, (4096, 4096), 1.0)
+    _, dt = _timed(lambda: oracle.gemm(As, Ws, 16))
+    out["sweep_p1_s"] = round(dt, 3)
+    out["sweep_p1_tflops"] = round(2.0 * 4096 ** 3 / dt / 1e12, 4)
+    del Ws, As
+    _, dt = _timed(lambda: oracle.moe(mc["X"], mc["logits"], mc["Wg"], mc["Wu"], mc["Wd"],
+                                      mc["top_k"], mc["leaves_gate_up"], mc["leaves_down"]))
+    out["moe_s"] = round(dt, 3)
+    out["moe_tokens_per_s"] = round(mc["T"] / dt, 1)
+    # one thread: a row sample of the prefill GEMM sized from a 16-row run
+    n_all = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        _, dt = _timed(lambda: oracle.gemm(cfg["A"][:16], cfg["Wt"], cfg["leaves"]))
+        r1 = int(min(cfg["M"], max(16, 16 * single_s / max(dt, 1e-6))))
+        _, dt = _timed(lambda: oracle.gemm(cfg["A"][:r1], cfg["Wt"], cfg["leaves"]))
+    finally:
+        oracle.set_threads(n_all)
+    out["single_thread"] = {"value": 2.0 * r1 * cfg["N"] * cfg["K"] / dt / 1e12, "unit": "TFLOP/s",
+                            "cores": 1, "sample": f"{r1} rows of the prefill GEMM, {dt:.1f} s"}
+    return out, lp, rows
+
+
+def _pcts(x):
+    x = np.asarray(x, dtype=np.float64)
+    return {"p50": float(np.percentile(x, 50)), "p95": float(np.percentile(x, 95)),
+            "p99": float(np.percentile(x, 99)), "max": float(np.max(x))}
+
+
+def _parity(cfg, c2_rows, c2_cols, c2_gpu, lm_rows, c3_gpu, c3_oracle):
+    """|gpu - oracle| over the sampled prefill-GEMM elements (FP32 roots) and
+    the sampled LM-head rows, with the largest error / tolerance."""
+    import oracle
+    from iso_synth import bf16_bits_to_f32
+    want = oracle.gemm_elems(cfg["A"], cfg["Wt"], cfg["leaves"], c2_rows, c2_cols).astype(np.float64)
+    a = np.abs(bf16_bits_to_f32(cfg["A"][c2_rows]).astype(np.float64))
+    w = np.abs(bf16_bits_to_f32(cfg["Wt"][c2_cols]).astype(np.float64))
+    tol = 1e-5 * np.einsum("ik,ik->i", a, w)
+    err = np.abs(c2_gpu.astype(np.float64) - want)
+    lerr = np.abs(c3_gpu.astype(np.float64) - c3_oracle)
+    assert np.array_equal(lm_rows, np.sort(lm_rows))
+    return {"prefill": {"elements": int(err.size), "abs_err": _pcts(err),
+                        "max_err_over_tol": float(np.max(err / tol)),
+                        "tolerance": "1e-5 * sum_k |a_k b_k| per element"},
+            "lmhead": {"rows": int(lerr.size), "abs_err": _pcts(lerr),
+                       "max_err_over_tol": float(np.max(lerr) / 1e-5),
+                       "tolerance": "1e-5 absolute per logprob"}}
 
 
 def main():
@@ -214,6 +297,7 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    ok = True
     # ---------------- cost of invariance on the same shape
     outb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     base = lambda: iso.gemm_baseline(A, W, out=outb, out_dtype=iso.BF16)
@@ -232,11 +316,24 @@ def main():
         "invariance_overhead_vs_baseline": round(kern_ms / b_ms - 1.0, 4),
         "invariance_overhead_vs_torch": round(kern_ms / t_ms - 1.0, 4),
     }
+    # FP32 roots of sampled elements for the |gpu - oracle| figures (same bits
+    # as the bf16 output before its rounding)
+    rng = np.random.default_rng(2024)
+    c2_rows = rng.integers(0, M, 4096)
+    c2_cols = rng.integers(0, N, 4096)
+    outf = iso.gemm(A, W, c, out_dtype=iso.F32)
+    torch.cuda.synchronize()
+    c2_gpu = outf[torch.from_numpy(c2_rows).to("cuda"), torch.from_numpy(c2_cols).to("cuda")].cpu().numpy()
+    ok &= bool(torch.equal(outf.to(torch.bfloat16).view(torch.int16), out.view(torch.int16)))
+    del outf
+    extra["workspace_bytes"] = {
+        "prefill_p1": iso.gemm_workspace(c, M, N, 1),
+        "prefill_p8": iso.gemm_workspace(c, M, N, 8),
+    }
     # bitwise: rows alone / in the batch, and 1 vs 8 partitions
     ref = out.clone()
     alone = torch.empty((8, N), dtype=torch.bfloat16, device="cuda")
     rows = [0, 1, 127, 128, 2048, 4000, 4094, 4095]
-    ok = True
     for i, r in enumerate(rows):
         iso.gemm(A[r:r + 1].contiguous(), W, c, out=alone[i:i + 1], out_dtype=iso.BF16)
     torch.cuda.synchronize()
@@ -264,10 +361,25 @@ def main():
         ms8 = _time_events(g8, max(5, args.steps // 5), stream)
         ok &= bool(torch.equal(outs.view(torch.int32), ref_s.view(torch.int32)))
         fs = 2.0 * 4096 * 4096 * Ks
+        # the cost of invariance at this shape: one accumulator over all of K
+        # on the same tiles, and torch's linear layer (hipBLASLt, bf16 out)
+        outsb = torch.empty_like(outs)
+        gb = lambda: iso.gemm_baseline(As, Ws, out=outsb)
+        gb()
+        msb = _time_events(gb, max(5, args.steps // 5), stream)
+        gt = lambda: torch.nn.functional.linear(As, Ws)
+        gt()
+        mst = _time_events(gt, max(5, args.steps // 5), stream)
+        del outsb
         extra["sweep"] = {"shape": "4096x4096x4096, 16 leaves of 256, fp32 out",
                           "p1_tflops": round(fs / (ms1 * 1e-3) / 1e12, 2),
                           "p8_tflops": round(fs / (ms8 * 1e-3) / 1e12, 2),
-                          "p1_ms": round(ms1, 4), "p8_ms": round(ms8, 4)}
+                          "p1_ms": round(ms1, 4), "p8_ms": round(ms8, 4),
+                          "baseline_tflops": round(fs / (msb * 1e-3) / 1e12, 2),
+                          "torch_linear_tflops": round(fs / (mst * 1e-3) / 1e12, 2),
+                          "invariance_overhead_vs_baseline": round(ms1 / msb - 1.0, 4),
+                          "invariance_overhead_vs_torch": round(ms1 / mst - 1.0, 4)}
+        extra["workspace_bytes"]["sweep_p8"] = iso.gemm_workspace(cs, 4096, 4096, 8)
         # one row per call (a decode step of the same layer): the weights streamed once
         A1 = As[:1].contiguous()
         o1 = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
@@ -277,7 +389,18 @@ def main():
         ok &= bool(torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
         extra["sweep"]["row1_us"] = round(ms_1 * 1e3, 2)
         extra["sweep"]["row1_weight_gbs"] = round(4096 * Ks * 2 / (ms_1 * 1e-3) / 1e9, 1)
-        del Ws, As, outs, ws8, ref_s, A1, o1
+        # batches of 8 and 64 rows of the same layer (the sweep's other batch
+        # sizes); rows 100.. of the 4096-row batch, so the bits must match it
+        for mb in (8, 64):
+            Ab = As[100:100 + mb].contiguous()
+            ob = torch.empty((mb, 4096), dtype=torch.float32, device="cuda")
+            g_b = lambda: iso.gemm(Ab, Ws, cs, out=ob)
+            g_b()
+            ms_b = _time_events(g_b, max(10, args.steps), stream)
+            ok &= bool(torch.equal(ob.view(torch.int32), ref_s[100:100 + mb].view(torch.int32)))
+            extra["sweep"][f"rows{mb}_us"] = round(ms_b * 1e3, 2)
+            extra["sweep"][f"rows{mb}_weight_gbs"] = round(4096 * Ks * 2 / (ms_b * 1e-3) / 1e9, 1)
+        del Ws, As, outs, ws8, ref_s, A1, o1, Ab, ob
 
         # ---------------- LM-head logprob
         lm = make_config("lmhead")
@@ -303,6 +426,37 @@ def main():
                            "ms": round(lm_ms, 4),
                            "tflops": round(lm_flop / (lm_ms * 1e-3) / 1e12, 2),
                            "mfma_frac": round(lm_flop / (lm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        # the cost of invariance at this shape: the fused kernel with one
+        # accumulator per logit (no leaf tree), and torch's unconstrained path
+        # (linear layer to bf16 logits, FP32 log_softmax, gather)
+        cl1 = iso.contract(1, lm["K"], iso.VOCAB_CHUNK)
+        lp1l = torch.empty_like(lp)
+        run_l1 = lambda: iso.lmhead_logprob(H, Wv, tok, cl1, out=lp1l, workspace=wsl)
+        run_l1()
+        l1_ms = _time_events(run_l1, max(3, args.steps // 10), stream)
+        tokl = tok.long().unsqueeze(1)
+
+        def run_tl():
+            z = torch.nn.functional.linear(H, Wv)
+            return torch.log_softmax(z.float(), dim=-1).gather(1, tokl)
+        run_tl()
+        tl_ms = _time_events(run_tl, 3, stream)
+        tlin = lambda: torch.nn.functional.linear(H, Wv)
+        tlin()
+        tlin_ms = _time_events(tlin, 3, stream)
+        lp_t = run_tl().squeeze(1)
+        torch.cuda.synchronize()
+        extra["lmhead"].update({
+            "one_leaf_ms": round(l1_ms, 4),
+            "torch_linear_logsoftmax_gather_ms": round(tl_ms, 4),
+            "torch_linear_only_ms": round(tlin_ms, 4),
+            "invariance_overhead_vs_one_leaf": round(lm_ms / l1_ms - 1.0, 4),
+            "invariance_overhead_vs_torch": round(lm_ms / tl_ms - 1.0, 4),
+            "torch_bf16_logits_max_abs_diff": round(float((lp_t - lp_ref).abs().max()), 6)})
+        del lp1l, lp_t
+        extra["workspace_bytes"]["lmhead"] = iso.lmhead_workspace(cl, lm["M"], lm["V"], 1)
+        lm_rows = np.sort(np.random.default_rng(2025).choice(lm["M"], 64, replace=False))
+        c3_gpu = lp_ref[torch.from_numpy(lm_rows).to("cuda")].cpu().numpy()
         # the same layer split over 8 vocabulary shards (stats exchange + final tree)
         nch = (lm["V"] + 127) // 128
         st8 = torch.empty((lm["M"], nch, 2), dtype=torch.float32, device="cuda")
@@ -354,12 +508,49 @@ def main():
         torch.cuda.synchronize()
         ok &= bool(torch.equal(yr.view(torch.int32), y_ref[rev].view(torch.int32)))
         moe_flop = 2.0 * T * k * (2 * Hd * I + I * Hd)
+        # the cost of invariance: the same kernels with one accumulator per
+        # output (one leaf over all of K), and a plain torch expert loop that
+        # scatters with index_add_ (atomics: the usual non-invariant MoE)
+        cg1 = iso.contract(1, Hd, 0)
+        cd1 = iso.contract(1, I, 0)
+        y1 = torch.empty_like(y)
+        run_m1 = lambda: iso.moe_combine(X, lgt, Wg, Wu, Wd, k, cg1, cd1, out=y1, workspace=wsm)
+        run_m1()
+        m1_ms = _time_events(run_m1, max(3, args.steps // 5), stream)
+        def run_mt():
+            p_ = torch.softmax(lgt, dim=-1)
+            gv, gi = torch.topk(p_, k, dim=-1)
+            gv = (gv / gv.sum(dim=-1, keepdim=True)).reshape(-1)
+            flat = gi.reshape(-1)
+            order = torch.argsort(flat, stable=True)
+            counts = torch.bincount(flat, minlength=E).tolist()
+            yt = torch.zeros((T, Hd), dtype=torch.float32, device="cuda")
+            off = 0
+            for e in range(E):
+                seg = order[off:off + counts[e]]
+                off += counts[e]
+                if seg.numel() == 0:
+                    continue
+                ts = seg // k
+                xe = X[ts]
+                g = torch.nn.functional.linear(xe, Wg[e])
+                u = torch.nn.functional.linear(xe, Wu[e])
+                oe = torch.nn.functional.linear(torch.nn.functional.silu(g) * u, Wd[e]).float()
+                yt.index_add_(0, ts, oe * gv[seg].unsqueeze(1))
+            return yt
+        run_mt()
+        mt_ms = _time_events(run_mt, 3, stream)
         extra["moe"] = {"shape": "4096 tokens, hidden 2048, 128 experts, top-8, SwiGLU 512, "
                                  "4 leaves (gate/up 4x512, down 4x128)",
                         "ms": round(moe_ms, 4),
                         "tokens_per_s": round(T / (moe_ms * 1e-3), 1),
-                        "tflops": round(moe_flop / (moe_ms * 1e-3) / 1e12, 2)}
-        del X, lgt, Wg, Wu, Wd, y, wsm, yr
+                        "tflops": round(moe_flop / (moe_ms * 1e-3) / 1e12, 2),
+                        "one_leaf_ms": round(m1_ms, 4),
+                        "torch_expert_loop_ms": round(mt_ms, 4),
+                        "invariance_overhead_vs_one_leaf": round(moe_ms / m1_ms - 1.0, 4),
+                        "invariance_overhead_vs_torch_loop": round(moe_ms / mt_ms - 1.0, 4)}
+        extra["workspace_bytes"]["moe"] = iso.moe_workspace(T, Hd, E, I, k)
+        del X, lgt, Wg, Wu, Wd, y, wsm, yr, y1
 
         # ---------------- RMSNorm with residual add in front of the LM-head
         Mn, Hn = 8192, 2048
@@ -431,7 +622,12 @@ def main():
     line["bitwise_pass"] = ok
     line["sub"] = extra
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = _cpu_baseline(cfg)
+        cb = _cpu_baseline(cfg)
+        more, c3_oracle, rows_or = _cpu_more(cfg, lm, mc)
+        assert np.array_equal(rows_or, lm_rows)
+        cb["workloads"] = more
+        line["cpu_baseline"] = cb
+        extra["parity"] = _parity(cfg, c2_rows, c2_cols, c2_gpu, lm_rows, c3_gpu, c3_oracle)
     print(json.dumps(line), flush=True)
 
 

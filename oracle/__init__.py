@@ -47,6 +47,7 @@ def _load():
         I = ctypes.c_int
         sigs = {
             "oracle_threads": ([], I),
+            "oracle_set_threads": ([I], I),
             "oracle_gemm": ([P, P, I64, I64, I64, I, P], I),
             "oracle_gemm_elems": ([P, P, I64, I, P, P, I64, P], I),
             "oracle_gemm_partitioned": ([P, P, I64, I64, I64, I, I, P], I),
@@ -86,6 +87,12 @@ def _check(rc, what):
 
 def threads() -> int:
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the following calls (they split independent outputs only,
+    so no result changes)."""
+    _check(_load().oracle_set_threads(int(n)), "set_threads")
 
 
 def gemm(A, Wt, leaves: int) -> np.ndarray:

@@ -127,6 +127,18 @@ int oracle_threads(void)
 #endif
 }
 
+/* Thread count of the following calls (n >= 1); no effect on any result,
+ * since threads only split independent outputs. */
+int oracle_set_threads(int n)
+{
+    if (n < 1)
+        return -1;
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#endif
+    return 0;
+}
+
 /* One leaf: sequential FP32 sum over k in [k0, k1), ascending. */
 static float leaf_dot(const float *a, const uint16_t *w, int64_t k0, int64_t k1)
 {
