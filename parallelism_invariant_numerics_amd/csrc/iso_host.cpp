@@ -44,6 +44,63 @@ int internal_parts(const iso_contract *c, int partitions)
     return lpp > kMaxLeavesPerTile ? (int)c->leaf_count / kMaxLeavesPerTile : partitions;
 }
 
+// How an iso_gemm call runs.  The choice follows the call's shape (and
+// whether a workspace was given), never the numbers, and every choice gives
+// the same bits: the rows kernel, the tile kernel and the partition path
+// all compute each leaf with the same MFMA chain and combine the leaves
+// with the same tree.
+//   rows   a few rows: one workgroup per 16 output columns streaming the
+//          weights (gemm_rows.hip)
+//   parts  partition roots of `parts` contiguous leaf blocks into the
+//          workspace, then the top tree levels (parts == 1: the tile kernel
+//          writes the output directly)
+struct GemmPlan {
+    bool rows;
+    int parts;
+};
+
+constexpr int64_t kCus = 256;
+constexpr int64_t kSmallLayerBytes = (int64_t)8 << 20;
+
+int64_t tile_count(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
+
+// P = 1 calls whose output has too few 128 x 128 tiles to fill the chip may
+// split K into more partitions (whole subtrees, so the same bits) when the
+// caller gives a workspace: the smallest power of two up to 4 that brings
+// the workgroups to one per CU.  (Measured at 33-256 rows of 4096 x 4096
+// with 16 leaves, 2048 x 2048 with 8 and 4096 x 2048 with 4: four
+// partitions of eight-wave workgroups beat eight of the two-per-CU shape.)
+int split_parts(const iso_contract *c, int64_t M, int64_t N)
+{
+    const int64_t tiles = tile_count(M, N);
+    int p = internal_parts(c, 1);
+    if (tiles >= kCus / 2)
+        return p;
+    while (p < 4 && 2 * p <= (int)c->leaf_count && tiles * p < kCus)
+        p *= 2;
+    return p;
+}
+
+GemmPlan plan_gemm(const iso_contract *c, int64_t M, int64_t N, int64_t K, int partitions,
+                   bool have_ws)
+{
+    const int L = (int)c->leaf_count;
+    const bool rows_ok =
+        partitions == 1 && iso::gemm_rows_supported(M, K, L, (int)c->leaf_size);
+    if (partitions != 1)
+        return {false, internal_parts(c, partitions)};
+    // weight streaming wins while the rows are few, or the layer is small
+    // enough that a second launch would cost more than the rows' re-reads
+    if (rows_ok && (M <= 32 || (M <= 64 && L >= 8 && N * K * 2 <= kSmallLayerBytes)))
+        return {true, 1};
+    const int split = split_parts(c, M, N);
+    if (split > internal_parts(c, 1) && have_ws)
+        return {false, split};
+    if (rows_ok && M <= 96 && L >= 8 && tile_count(M, N) < kCus / 2)
+        return {true, 1};
+    return {false, internal_parts(c, 1)};
+}
+
 thread_local hipError_t g_last_launch_error = hipSuccess;
 
 iso_status launch_status(hipError_t e)
@@ -198,7 +255,8 @@ size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int parti
         return (size_t)-1;
     if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim)
         return (size_t)-1;
-    int parts = internal_parts(c, partitions);
+    const int64_t K = (int64_t)c->leaf_count * c->leaf_size;
+    const int parts = plan_gemm(c, M, N, K, partitions, true).parts;
     return parts > 1 ? (size_t)parts * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -221,8 +279,13 @@ iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *
         return ISO_OK;
     if (!A || !Wt || !C || !aligned16(A) || !aligned16(Wt))
         return ISO_ERR_ARG;
-    const int parts = internal_parts(c, partitions);
-    const size_t need = iso_gemm_workspace(c, M, N, partitions);
+    // a P = 1 call may take the split-K plan only with a workspace big
+    // enough for it; without one it runs another plan with the same bits
+    const size_t split_need = iso_gemm_workspace(c, M, N, partitions);
+    const bool have_ws = workspace && workspace_bytes >= split_need;
+    const GemmPlan plan = plan_gemm(c, M, N, K, partitions, have_ws);
+    const int parts = plan.parts;
+    const size_t need = parts > 1 ? (size_t)parts * (size_t)M * (size_t)N * sizeof(float) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return ISO_ERR_WORKSPACE;
 
@@ -230,13 +293,10 @@ iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int lpp = (int)c->leaf_count / parts;
     const int bf16 = out_dtype == ISO_BF16;
-    if (partitions == 1) {  // a few rows: the weight-streaming kernel, same bits
-        const hipError_t r = iso::launch_gemm_rows(
+    if (plan.rows)
+        return launch_status(iso::launch_gemm_rows(
             static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Wt), C, bf16, M, N, K,
-            (int)c->leaf_count, (int)c->leaf_size, st);
-        if (r != hipErrorNotSupported)
-            return launch_status(r);
-    }
+            (int)c->leaf_count, (int)c->leaf_size, st));
     if (parts == 1)
         return launch_status(iso::launch_gemm_partials(
             static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Wt), C, bf16 ? 1 : 0,

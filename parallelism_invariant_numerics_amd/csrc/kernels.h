@@ -20,8 +20,10 @@ hipError_t launch_gemm_partials(const uint16_t *A, const uint16_t *Wt, void *out
                                 int64_t M, int64_t N, int64_t K, int leaves_per_part,
                                 int leaf_size, int parts, hipStream_t stream);
 
-// The same GEMM for M <= 32 rows, one partition, 4-64 leaves of 64-512
+// The same GEMM for up to 256 rows, one partition, 4-64 leaves of 64-512
 // columns, K <= 4096 (gemm_rows.hip); hipErrorNotSupported otherwise.
+// gemm_rows_supported says whether a call shape qualifies.
+bool gemm_rows_supported(int64_t M, int64_t K, int leaves, int leaf_size);
 hipError_t launch_gemm_rows(const uint16_t *A, const uint16_t *Wt, void *out, int out_bf16,
                             int64_t M, int64_t N, int64_t K, int leaves, int leaf_size,
                             hipStream_t stream);

@@ -112,8 +112,19 @@ def test_gemm_workspace_sizes():
     for P in (2, 4, 8):
         assert iso.gemm_workspace(c16, 10, 20, P) == P * 10 * 20 * 4
     # a partition deeper than the register tree is split further internally
-    assert iso.gemm_workspace(iso.contract(64, 64, 0), 10, 20, 1) == 4 * 10 * 20 * 4
-    assert iso.gemm_workspace(iso.contract(32, 64, 0), 10, 20, 1) == 2 * 10 * 20 * 4
+    # (a few rows take the weight-streaming kernel, which holds the whole tree)
+    assert iso.gemm_workspace(iso.contract(64, 64, 0), 10, 20, 1) == 0
+    assert iso.gemm_workspace(iso.contract(64, 64, 0), 1000, 4096, 1) == 4 * 1000 * 4096 * 4
+    assert iso.gemm_workspace(iso.contract(32, 64, 0), 1000, 4096, 1) == 2 * 1000 * 4096 * 4
+    # one partition on too few 128 x 128 tiles to fill the chip: an optional
+    # workspace lets the call split K into up to 8 subtrees (same bits)
+    assert iso.gemm_workspace(c16, 64, 4096, 1) == 4 * 64 * 4096 * 4
+    assert iso.gemm_workspace(iso.contract(8, 256, 0), 100, 2048, 1) == 4 * 100 * 2048 * 4
+    assert iso.gemm_workspace(iso.contract(2, 1024, 0), 100, 2048, 1) == 2 * 100 * 2048 * 4
+    assert iso.gemm_workspace(iso.contract(4, 512, 0), 300, 4096, 1) == 4 * 300 * 4096 * 4
+    assert iso.gemm_workspace(c16, 4096, 4096, 1) == 0
+    # small layers keep the weight-streaming kernel up to 64 rows
+    assert iso.gemm_workspace(iso.contract(8, 256, 0), 64, 2048, 1) == 0
     with pytest.raises(iso.IsoError):
         iso.gemm_workspace(c16, 10, 20, 3)
 

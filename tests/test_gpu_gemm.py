@@ -7,6 +7,8 @@
 * the prefill workload at full size (4096 x 2048 x 2048, 8 leaves of 256):
   sampled elements against the oracle, all elements across P and output dtypes.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -191,19 +193,35 @@ def test_partition_combine_shapes(M, N):
                                    (4096, 16, 4096), (2048, 32, 130), (4096, 64, 96),
                                    (4096, 8, 256), (4096, 4, 256), (1024, 2, 200)])
 def test_few_rows_match_batch(K, L, N):
-    """One to 32 rows take the weight-streaming kernel (one workgroup per 16 output columns,
-    eight subtrees of leaves per column block); the same rows inside a batch of 200 take the
-    tile kernel.  Same bits, FP32 and bf16, ragged N; 4 leaves of 1024 and 2 leaves are shapes
-    it leaves to the tile kernels."""
-    A = normal_bf16(K + N, (200, K), 1.0)
+    """Up to 256 rows may take the weight-streaming kernel (one workgroup per 16 output
+    columns, eight subtrees of leaves per column block, row groups of 16 double-buffered), or,
+    with a workspace on a shape of few 128 x 128 tiles, the tile kernel split into up to 8
+    partitions of whole subtrees; the same rows inside a batch of 600 take the tile kernel.
+    Same bits for every plan, FP32 and bf16, ragged N; 4 leaves of 1024 and 2 leaves are
+    shapes the weight-streaming kernel leaves to the tile kernels."""
+    t = torch()
+    A = normal_bf16(K + N, (600, K), 1.0)
     Wt = normal_bf16(K + N + 1, (N, K), 0.02)
     note(f"few rows vs batch K={K} L={L} N={N}")
     big = u32(_run(A, Wt, L))
     bigb = _run(A, Wt, L, 1, iso.BF16)
-    for m in (1, 5, 16, 17, 32):
+    c = iso.contract(L, K // L, 0)
+    dW = dev(Wt)
+    for m in (1, 5, 16, 17, 32, 33, 48, 64, 65, 96, 130, 256):
         for start in (0, 150):
+            a = dev(A[start:start + m])
             assert np.array_equal(u32(_run(A[start:start + m], Wt, L)), big[start:start + m]), (m, start)
             assert np.array_equal(_run(A[start:start + m], Wt, L, 1, iso.BF16),
                                   bigb[start:start + m]), (m, start)
+            # without a workspace (no split plan) the bits are the same
+            o = t.empty((m, N), dtype=t.float32, device="cuda")
+            st = iso.lib.iso_gemm(ctypes.byref(c), a.data_ptr(), dW.data_ptr(), o.data_ptr(), iso.F32,
+                                  m, N, K, 1, None, 0, t.cuda.current_stream().cuda_stream)
+            if st == 6:  # more than 16 leaves outside the weight-streaming kernel need one
+                assert L > 16, (m, start)
+                continue
+            assert st == 0, (m, start, st)
+            t.cuda.synchronize()
+            assert np.array_equal(u32(host(o)), big[start:start + m]), (m, start, "no workspace")
     check_gemm_tol(big[:16].view(np.float32), oracle.gemm(A[:16], Wt, L), absdot(A[:16], Wt),
                    f"few rows {K}/{L}")
