@@ -36,6 +36,16 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(out_path: str) -> str:
+    """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer
+    (same arithmetic flags), for the CPU sanitizer run of the tests."""
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-g"]
+    flags = [f for f in CFLAGS if f != "-O2"] + ["-O1"]
+    subprocess.run(["gcc", *flags, *san, _SRC, "-o", out_path, "-lm"], check=True)
+    return out_path
+
+
 def _load():
     global _lib
     if _lib is None:

@@ -63,5 +63,21 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# CPU build of the host code under AddressSanitizer and UndefinedBehavior-
+# Sanitizer: the C ABI's checks, the identities and SHA-256, with the kernel
+# launchers replaced by stubs that launch nothing (host_stubs.cpp).  g++ on
+# host sources only; no GPU code is built with a sanitizer.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer", "-g", "-O1"]
+
+
+def build_host_sanitized(out_path: str) -> str:
+    srcs = [os.path.join(CSRC, f) for f in HOST_SOURCES + ["host_stubs.cpp"]]
+    _run(["g++", "-std=c++17", "-fPIC", "-shared", "-Wall", *SANITIZE, "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", *srcs,
+          "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", out_path])
+    return out_path
+
+
 if __name__ == "__main__":
     build(verbose=True)

@@ -7,6 +7,7 @@
 // partition ("emulated rank") p of P owns leaves [p L/P, (p+1) L/P); its
 // workgroups write that subtree's root, and the combine kernel applies the
 // top log2(P) levels of the same tree, so every P gives the same bits.
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_core.hpp"
@@ -16,18 +17,20 @@ namespace iso {
 
 int device_cus()
 {
-    static int cache[64] = {};
+    // one entry per device; threads that race to fill an entry store the
+    // same value, and the atomic keeps every read whole
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 enum OutMode : int { kOutF32 = 0, kOutBF16 = 1, kOutWorkspace = 2 };

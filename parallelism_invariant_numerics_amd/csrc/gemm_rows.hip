@@ -25,8 +25,6 @@
 
 namespace iso {
 
-constexpr int kRowsMax = 256;
-constexpr int64_t kRowsMaxK = 4096;
 
 // The per-wave state of one column block: its weight fragments (all of its
 // subtree's K range) and where its rows and outputs are.
@@ -196,19 +194,6 @@ static hipError_t rows_ks(int ks, const uint16_t *A, const uint16_t *Wt, void *o
     default: break;
     }
     return hipErrorNotSupported;
-}
-
-bool gemm_rows_supported(int64_t M, int64_t K, int leaves, int leaf_size)
-{
-    if (M < 1 || M > kRowsMax || K > kRowsMaxK || leaf_size % 32 != 0)
-        return false;
-    const int ks = leaf_size / 32;
-    if (static_cast<int64_t>(ks) * 32 * leaves != K)
-        return false;
-    const int lw = leaves == 4 ? 1 : leaves / 8;  // leaves per wave
-    if (leaves != 4 && leaves != 8 && leaves != 16 && leaves != 32 && leaves != 64)
-        return false;
-    return (ks == 2 || ks == 4 || ks == 8 || ks == 16) && lw * ks <= 16;
 }
 
 hipError_t launch_gemm_rows(const uint16_t *A, const uint16_t *Wt, void *out, int out_bf16,

@@ -152,6 +152,26 @@ iso_status check_gemm_dims(int64_t M, int64_t N)
 
 }  // namespace
 
+namespace iso {
+
+// The shapes the weight-streaming kernel takes: whole 32-column k-steps,
+// four leaves (two column blocks of four subtrees) or 8-64 leaves (eight
+// subtrees), at most 16 k-steps per wave.
+bool gemm_rows_supported(int64_t M, int64_t K, int leaves, int leaf_size)
+{
+    if (M < 1 || M > kRowsMax || K > kRowsMaxK || leaf_size % 32 != 0)
+        return false;
+    const int ks = leaf_size / 32;
+    if (static_cast<int64_t>(ks) * 32 * leaves != K)
+        return false;
+    if (leaves != 4 && leaves != 8 && leaves != 16 && leaves != 32 && leaves != 64)
+        return false;
+    const int lw = leaves == 4 ? 1 : leaves / 8;  // leaves per wave
+    return (ks == 2 || ks == 4 || ks == 8 || ks == 16) && lw * ks <= 16;
+}
+
+}  // namespace iso
+
 extern "C" {
 
 iso_status iso_contract_init(iso_contract *c, uint32_t leaf_count, uint32_t leaf_size,

@@ -20,9 +20,12 @@ hipError_t launch_gemm_partials(const uint16_t *A, const uint16_t *Wt, void *out
                                 int64_t M, int64_t N, int64_t K, int leaves_per_part,
                                 int leaf_size, int parts, hipStream_t stream);
 
-// The same GEMM for up to 256 rows, one partition, 4-64 leaves of 64-512
-// columns, K <= 4096 (gemm_rows.hip); hipErrorNotSupported otherwise.
-// gemm_rows_supported says whether a call shape qualifies.
+// The same GEMM for up to kRowsMax rows, one partition, 4-64 leaves of
+// 64-512 columns, K <= kRowsMaxK (gemm_rows.hip); hipErrorNotSupported
+// otherwise.  gemm_rows_supported (host code) says whether a shape
+// qualifies.
+constexpr int64_t kRowsMax = 256;
+constexpr int64_t kRowsMaxK = 4096;
 bool gemm_rows_supported(int64_t M, int64_t K, int leaves, int leaf_size);
 hipError_t launch_gemm_rows(const uint16_t *A, const uint16_t *Wt, void *out, int out_bf16,
                             int64_t M, int64_t N, int64_t K, int leaves, int leaf_size,
