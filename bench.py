@@ -112,6 +112,42 @@ def _time_events(fn, steps, stream):
     return start.elapsed_time(end) / steps
 
 
+def _time_graph(fn, inner=20, replays=10, check=None, reset=None):
+    """Average duration (ms) of one fn() call replayed from a HIP graph of
+    `inner` back-to-back calls: the GPU time of a call without the Python
+    launch path (what a serving loop that replays graphs sees).  fn must not
+    allocate.  Returns None if capture is not available."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(inner):
+                fn()
+        if reset is not None:
+            reset()  # eager work between the capture and the replay: the replay must redo it
+        g.replay()
+        torch.cuda.synchronize()
+        if check is not None and not check():
+            return float("nan")  # a replay that changes the bits is reported, not timed
+        _settle(g.replay, 0.66 * SETTLE_S)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(replays):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / (replays * inner)
+    except RuntimeError:
+        return None
+
+
 def _source_hash(files):
     h = hashlib.sha256()
     for f in files:
@@ -389,18 +425,30 @@ def main():
         ok &= bool(torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
         extra["sweep"]["row1_us"] = round(ms_1 * 1e3, 2)
         extra["sweep"]["row1_weight_gbs"] = round(4096 * Ks * 2 / (ms_1 * 1e-3) / 1e9, 1)
+        gr = _time_graph(g_1, reset=o1.zero_,
+                         check=lambda: torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
+        ok &= bool(torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
+        ok &= gr is None or gr == gr
+        extra["sweep"]["row1_graph_us"] = None if gr is None else round(gr * 1e3, 2)
         # batches of 8 and 64 rows of the same layer (the sweep's other batch
         # sizes); rows 100.. of the 4096-row batch, so the bits must match it
         for mb in (8, 64):
             Ab = As[100:100 + mb].contiguous()
             ob = torch.empty((mb, 4096), dtype=torch.float32, device="cuda")
-            g_b = lambda: iso.gemm(Ab, Ws, cs, out=ob)
+            wsb = torch.empty(max(1, iso.gemm_workspace(cs, mb, 4096, 1)), dtype=torch.uint8,
+                              device="cuda")
+            g_b = lambda: iso.gemm(Ab, Ws, cs, out=ob, workspace=wsb)
             g_b()
             ms_b = _time_events(g_b, max(10, args.steps), stream)
             ok &= bool(torch.equal(ob.view(torch.int32), ref_s[100:100 + mb].view(torch.int32)))
             extra["sweep"][f"rows{mb}_us"] = round(ms_b * 1e3, 2)
             extra["sweep"][f"rows{mb}_weight_gbs"] = round(4096 * Ks * 2 / (ms_b * 1e-3) / 1e9, 1)
-        del Ws, As, outs, ws8, ref_s, A1, o1, Ab, ob
+            gr = _time_graph(g_b, reset=ob.zero_, check=lambda: torch.equal(ob.view(torch.int32),
+                                                            ref_s[100:100 + mb].view(torch.int32)))
+            ok &= bool(torch.equal(ob.view(torch.int32), ref_s[100:100 + mb].view(torch.int32)))
+            ok &= gr is None or gr == gr
+            extra["sweep"][f"rows{mb}_graph_us"] = None if gr is None else round(gr * 1e3, 2)
+        del Ws, As, outs, ws8, ref_s, A1, o1, Ab, ob, wsb
 
         # ---------------- LM-head logprob
         lm = make_config("lmhead")
@@ -482,8 +530,13 @@ def main():
         run_d()
         d_ms = _time_events(run_d, max(10, args.steps), stream)
         ok &= bool(torch.equal(lp1.view(torch.int32), lp_ref[:1].view(torch.int32)))
+        gd = _time_graph(run_d, inner=10, reset=lp1.zero_,
+                         check=lambda: torch.equal(lp1.view(torch.int32), lp_ref[:1].view(torch.int32)))
+        ok &= bool(torch.equal(lp1.view(torch.int32), lp_ref[:1].view(torch.int32)))
+        ok &= gd is None or gd == gd
         extra["decode"] = {"lmhead_1row_us": round(d_ms * 1e3, 2),
-                           "lmhead_1row_weight_gbs": round(lm["V"] * lm["K"] * 2 / (d_ms * 1e-3) / 1e9, 1)}
+                           "lmhead_1row_weight_gbs": round(lm["V"] * lm["K"] * 2 / (d_ms * 1e-3) / 1e9, 1),
+                           "lmhead_1row_graph_us": None if gd is None else round(gd * 1e3, 2)}
         del st8, tg8, lp8s, lp1, ws1
         del H, Wv, tok, lp, wsl
 

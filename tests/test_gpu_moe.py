@@ -199,3 +199,29 @@ def test_bucket_paths_agree():
         note(f"moe bucket paths: {n} of them (64-token blocks)")
         ys, _ = _run(X[sel], lg[sel], Wg, Wu, Wd, k, 1, 1, dW)
         assert np.array_equal(ys.view(np.uint32), big[sel].view(np.uint32)), n
+
+
+def test_swiglu_entry_point():
+    # the expert activation on its own: h is bf16 of the returned FP32 activation bit
+    # for bit, and that activation is within a few FP32 roundings (the hardware exp2
+    # of a rounded -g log2 e adds |g| 2^-24 relative) of silu(g) u in float64
+    t = torch()
+    rng = np.random.default_rng(77)
+    g = (rng.standard_normal(100003) * 3.0).astype(np.float32)
+    u = (rng.standard_normal(100003) * 2.0).astype(np.float32)
+    g[:6] = [0.0, -0.0, 80.0, -80.0, 1e-30, -1e-30]
+    note("swiglu entry point")
+    act, h = iso.swiglu(t.from_numpy(g).cuda(), t.from_numpy(u).cuda())
+    act, h = host(act), host(h)
+    from iso_synth import f32_to_bf16_bits
+    assert np.array_equal(h, f32_to_bf16_bits(act))
+    g64, u64 = g.astype(np.float64), u.astype(np.float64)
+    want = g64 / (1.0 + np.exp(-g64)) * u64
+    tol = np.abs(want) * 2.0 ** -24 * (10.0 + np.abs(g64)) + 1e-37
+    assert np.all(np.abs(act.astype(np.float64) - want) <= tol)
+    assert act[0] == 0.0 and abs(act[3]) < 1e-30
+    # the h-only form and an empty call
+    h2 = iso.swiglu(t.from_numpy(g).cuda(), t.from_numpy(u).cuda(), act=False)
+    assert np.array_equal(host(h2), h)
+    e = iso.swiglu(t.empty(0, device="cuda"), t.empty(0, device="cuda"), act=False)
+    assert e.numel() == 0
