@@ -102,7 +102,9 @@ def _check_stages(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, y, st, what):
 
 
 @pytest.mark.parametrize("T,H,E,I,k,Lgu,Ldn", [(64, 256, 8, 128, 4, 4, 2), (37, 512, 16, 64, 2, 2, 1),
-                                               (130, 256, 64, 128, 8, 4, 2), (5, 128, 3, 192, 3, 1, 1)])
+                                               (130, 256, 64, 128, 8, 4, 2), (5, 128, 3, 192, 3, 1, 1),
+                                               (50, 1024, 8, 256, 4, 8, 4), (20, 2048, 4, 512, 2, 16, 8),
+                                               (300, 2048, 16, 512, 8, 4, 4)])
 def test_small_parity_by_stage(T, H, E, I, k, Lgu, Ldn):
     X = normal_bf16(T + 1, (T, H), 1.0)
     lg = normal_f32(T + 2, (T, E))
