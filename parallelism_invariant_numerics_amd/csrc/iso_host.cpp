@@ -525,7 +525,7 @@ MoeFull moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int top_k)
     o += align_up((size_t)E * (size_t)T * 4);
     l.max_tiles = (int)(E + (tk + 127) / 128);
     l.tiles = o;
-    o += align_up((size_t)l.max_tiles * 2 * 4);
+    o += align_up((size_t)l.max_tiles * 4 * 4);
     l.ntiles = o;
     o += 256;
     // per-block expert counts of the two-pass bucket (at most 16384 tokens)

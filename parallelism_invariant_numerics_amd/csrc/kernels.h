@@ -78,7 +78,7 @@ struct MoeBuffers {
     float *e;           // [T][k][H]
     int32_t *counts;    // [E]
     int32_t *rows;      // [E][T]: expert e's entries (token * k + slot) in token order, counts[e] of them
-    int32_t *tiles;     // [max_tiles][2]: (expert, first row within the expert)
+    int32_t *tiles;     // [max_tiles][4]: expert, first row within the expert, the expert's first tile, its tile count
     int32_t *ntiles;    // [1]
     int max_tiles;
     int32_t *blk_counts;  // [nblk][E] per 64-token block (two-pass bucket), or null

@@ -325,8 +325,9 @@ __global__ __launch_bounds__(1024) void moe_bucket_scatter_kernel(const int32_t 
 
 // ------------------------------------------------------------------ plan
 
-// Work list of (expert, first row) tiles in expert order: thread e (E <=
-// 1024 threads) scans the per-expert tile counts and writes its own tiles.
+// Work list of 128-row tiles in expert order, each (expert, first row, the
+// expert's first tile, its tile count): thread e (E <= 1024 threads) scans
+// the per-expert tile counts and writes its own tiles.
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *counts, int32_t *tiles,
                                                         int32_t *ntiles, int E)
 {
@@ -342,10 +343,13 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *counts, i
         scan[e] += add;
         __syncthreads();
     }
-    int n = scan[e] - mine;
+    const int first = scan[e] - mine;
+    int n = first;
     for (int m0 = 0; m0 < c; m0 += BM, ++n) {
-        tiles[2 * n] = e;
-        tiles[2 * n + 1] = m0;
+        tiles[4 * n] = e;
+        tiles[4 * n + 1] = m0;
+        tiles[4 * n + 2] = first;
+        tiles[4 * n + 3] = mine;
     }
     if (e == 1023)
         *ntiles = scan[1023];
@@ -380,10 +384,16 @@ __device__ __forceinline__ MoeTask moe_task(const int32_t *__restrict__ tiles,
                                             int tn_cols)
 {
     MoeTask t;
-    const int tile = w / ntn;
-    t.n0 = static_cast<int64_t>(w % ntn) * tn_cols;
-    t.e = __builtin_amdgcn_readfirstlane(tiles[2 * tile]);
-    t.m0 = __builtin_amdgcn_readfirstlane(tiles[2 * tile + 1]);
+    // an expert's tasks are contiguous, row tiles fastest: the tasks that
+    // share a weight column tile run next to each other (one L2)
+    const int q = w / ntn;
+    const int first = __builtin_amdgcn_readfirstlane(tiles[4 * q + 2]);
+    const int ntl = __builtin_amdgcn_readfirstlane(tiles[4 * q + 3]);
+    const int local = w - first * ntn;
+    const int tile = first + local % ntl;
+    t.n0 = static_cast<int64_t>(local / ntl) * tn_cols;
+    t.e = __builtin_amdgcn_readfirstlane(tiles[4 * tile]);
+    t.m0 = __builtin_amdgcn_readfirstlane(tiles[4 * tile + 1]);
     const int cnt = __builtin_amdgcn_readfirstlane(counts[t.e]);
     t.nvalid = cnt - t.m0 < BM ? cnt - t.m0 : BM;
     return t;
