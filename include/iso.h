@@ -211,8 +211,13 @@ iso_status iso_table_digests(const iso_composition *table, size_t n,
 iso_status iso_table_check(const iso_composition *table, size_t n, const char *region,
                            const char *case_name, const iso_contract *c, int partitions);
 
-/* Workspace bytes iso_gemm needs for this shape (0 when none); (size_t)-1
- * for arguments iso_gemm would reject. */
+/* Workspace bytes iso_gemm can use for this shape (0 when none); (size_t)-1
+ * for arguments iso_gemm would reject.  With P > 1 (or more than 16 leaves
+ * per partition outside the few-rows kernel) the workspace is required.
+ * With P = 1 on an output of fewer than 128 tiles of 128 x 128 and more
+ * than 32 rows, the size returned lets the call split K into up to four
+ * partitions of whole subtrees internally (same bits, more workgroups); a
+ * call given less runs without that split. */
 size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int partitions);
 
 /*
@@ -223,9 +228,12 @@ size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int parti
  * `partitions` P emulates P tensor-parallel ranks on this GPU: partition p
  * computes its subtree root into the workspace and a combine kernel applies
  * the top log2(P) levels.  Every P allowed by the claim gives the same bits.
- * The launch shape follows the problem (128 x 128 tiles; with P = 1 and at
- * most 32 rows, one workgroup per 16 output columns streaming the weights),
- * never the numbers: a row's bits do not depend on M or on its position.
+ * The launch shape follows the problem (128 x 128 tiles; with P = 1 and up
+ * to 32 rows -- or up to 96 rows without a workspace, 64 on a layer of at
+ * most 8 MiB of weights -- one workgroup per 16 output columns streaming the
+ * weights; with P = 1, a workspace and few output tiles, an internal split
+ * of K), never the numbers: a row's bits do not depend on M, on its
+ * position, or on which of these runs.
  * Limits: M, N < 2^23 and (M/128)(N/128) < 2^28 tiles, K <= 2^22.
  */
 iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *C,
