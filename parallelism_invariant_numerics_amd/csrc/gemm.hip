@@ -140,14 +140,21 @@ __global__ __launch_bounds__(256) void partition_combine4_kernel(const float *ws
 }
 
 // Trees of at most two leaves per workgroup fit the two-workgroups-per-CU
-// shape; deeper ones take the eight-wave shape.  Both give the same bits.
+// shape, which a grid of more workgroups than CUs fills best; deeper trees,
+// and grids of at most one workgroup per CU, take the eight-wave shape
+// (its deeper ring hides more of the load latency when a CU holds only one
+// workgroup).  Both give the same bits.
 template <int LOG>
 static hipError_t launch_leaf(const GemmParams &p, int parts, hipStream_t stream)
 {
-    using C = typename std::conditional<(LOG <= 1), CfgDual, CfgWide>::type;
     const int64_t tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
     dim3 grid(static_cast<unsigned>(tiles * parts));
-    hipLaunchKernelGGL((gemm_leaf_kernel<C, LOG>), grid, dim3(C::kThreads), 0, stream, p);
+    if (LOG <= 1 && tiles * parts > device_cus())
+        hipLaunchKernelGGL((gemm_leaf_kernel<CfgDual, LOG>), grid, dim3(CfgDual::kThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((gemm_leaf_kernel<CfgWide, LOG>), grid, dim3(CfgWide::kThreads), 0,
+                           stream, p);
     return hipGetLastError();
 }
 

@@ -66,17 +66,19 @@ int64_t tile_count(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127)
 
 // P = 1 calls whose output has too few 128 x 128 tiles to fill the chip may
 // split K into more partitions (whole subtrees, so the same bits) when the
-// caller gives a workspace: the smallest power of two up to 4 that brings
-// the workgroups to one per CU.  (Measured at 33-256 rows of 4096 x 4096
-// with 16 leaves, 2048 x 2048 with 8 and 4096 x 2048 with 4: four
-// partitions of eight-wave workgroups beat eight of the two-per-CU shape.)
+// caller gives a workspace: the smallest power of two that brings the
+// workgroups to one per CU, at most 8 partitions up to 64 rows and 4 above
+// (the partial roots then cost more to write and fold than the extra
+// workgroups gain; measured at 33-256 rows of 4096 x 4096 with 16 leaves,
+// 2048 x 2048 with 8 and 4096 x 2048 with 4).
 int split_parts(const iso_contract *c, int64_t M, int64_t N)
 {
     const int64_t tiles = tile_count(M, N);
     int p = internal_parts(c, 1);
     if (tiles >= kCus / 2)
         return p;
-    while (p < 4 && 2 * p <= (int)c->leaf_count && tiles * p < kCus)
+    const int cap = M <= 64 ? 8 : 4;
+    while (p < cap && 2 * p <= (int)c->leaf_count && tiles * p < kCus)
         p *= 2;
     return p;
 }

@@ -118,7 +118,8 @@ def test_gemm_workspace_sizes():
     assert iso.gemm_workspace(iso.contract(32, 64, 0), 1000, 4096, 1) == 2 * 1000 * 4096 * 4
     # one partition on too few 128 x 128 tiles to fill the chip: an optional
     # workspace lets the call split K into up to 8 subtrees (same bits)
-    assert iso.gemm_workspace(c16, 64, 4096, 1) == 4 * 64 * 4096 * 4
+    assert iso.gemm_workspace(c16, 64, 4096, 1) == 8 * 64 * 4096 * 4
+    assert iso.gemm_workspace(c16, 128, 4096, 1) == 4 * 128 * 4096 * 4
     assert iso.gemm_workspace(iso.contract(8, 256, 0), 100, 2048, 1) == 4 * 100 * 2048 * 4
     assert iso.gemm_workspace(iso.contract(2, 1024, 0), 100, 2048, 1) == 2 * 100 * 2048 * 4
     assert iso.gemm_workspace(iso.contract(4, 512, 0), 300, 4096, 1) == 4 * 300 * 4096 * 4
