@@ -91,9 +91,15 @@ GemmPlan plan_gemm(const iso_contract *c, int64_t M, int64_t N, int64_t K, int p
         partitions == 1 && iso::gemm_rows_supported(M, K, L, (int)c->leaf_size);
     if (partitions != 1)
         return {false, internal_parts(c, partitions)};
-    // weight streaming wins while the rows are few, or the layer is small
-    // enough that a second launch would cost more than the rows' re-reads
-    if (rows_ok && (M <= 32 || (M <= 64 && L >= 8 && N * K * 2 <= kSmallLayerBytes)))
+    // weight streaming wins while the rows are few (up to 16, one MFMA row
+    // block), and up to 32 rows on a layer small enough that the partition
+    // roots' round trip and the second launch cost more than the rows'
+    // re-reads; past that a split over the workspace, when there is one, is
+    // faster (measured: 17-32 rows of 4096 x 4096 with 16 leaves 11.1-13.1 ->
+    // 10.3-11.6 us, of 4096 x 2048 with 4 leaves 10.7-13.0 -> 8.9-9.6 us;
+    // 48-64 rows of 2048 x 2048 with 8 leaves 9.3-10.7 -> 8.4-8.9 us)
+    const bool small_layer = N * K * 2 <= kSmallLayerBytes;
+    if (rows_ok && (M <= 16 || (M <= 32 && (small_layer || !have_ws))))
         return {true, 1};
     const int split = split_parts(c, M, N);
     if (split > internal_parts(c, 1) && have_ws)

@@ -124,8 +124,11 @@ def test_gemm_workspace_sizes():
     assert iso.gemm_workspace(iso.contract(2, 1024, 0), 100, 2048, 1) == 2 * 100 * 2048 * 4
     assert iso.gemm_workspace(iso.contract(4, 512, 0), 300, 4096, 1) == 4 * 300 * 4096 * 4
     assert iso.gemm_workspace(c16, 4096, 4096, 1) == 0
-    # small layers keep the weight-streaming kernel up to 64 rows
-    assert iso.gemm_workspace(iso.contract(8, 256, 0), 64, 2048, 1) == 0
+    # the weight-streaming kernel takes up to 16 rows, and up to 32 on small layers
+    assert iso.gemm_workspace(iso.contract(8, 256, 0), 32, 2048, 1) == 0
+    assert iso.gemm_workspace(iso.contract(8, 256, 0), 64, 2048, 1) == 8 * 64 * 2048 * 4
+    assert iso.gemm_workspace(c16, 16, 4096, 1) == 0
+    assert iso.gemm_workspace(c16, 32, 4096, 1) == 8 * 32 * 4096 * 4
     with pytest.raises(iso.IsoError):
         iso.gemm_workspace(c16, 10, 20, 3)
 
