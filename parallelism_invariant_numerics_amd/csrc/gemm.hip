@@ -11,6 +11,7 @@
 #include <type_traits>
 
 #include "gemm_core.hpp"
+#include "gemm_wide.hpp"
 #include "kernels.h"
 
 namespace iso {
@@ -83,6 +84,37 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_leaf_kernel(GemmParams p)
     }
 }
 
+// The same contraction on 128 x 256 tiles (at most four leaves per
+// workgroup, one wave per SIMD); same tile order with column groups of the
+// same width in columns.
+template <int LOG>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(GemmParams p)
+{
+    __shared__ __attribute__((aligned(16))) char lds[kWLdsBytes];
+    const int tm = static_cast<int>((p.M + BM - 1) / BM);
+    const int tn = static_cast<int>((p.N + WBN - 1) / WBN);
+    const int ntile = tm * tn;
+    const int part = blockIdx.x / ntile;
+    int mt, nt;
+    xcd_tile(blockIdx.x % ntile, ntile, tn, tm, kTileGroup * BN / WBN, nt, mt);
+    const int64_t m0 = static_cast<int64_t>(mt) * BM;
+    const int64_t n0 = static_cast<int64_t>(nt) * WBN;
+    const PipeW pipe = make_pipe_w(p.A + m0 * p.K, p.M - m0, p.Wt + n0 * p.K, p.N - n0, p.K,
+                                   part * p.k_per_part);
+    AccW root;
+    leaf_tree_mainloop_w<LOG>(pipe, p.stages_per_leaf, lds, root);
+    if (p.mode == kOutWorkspace) {
+        float *ws = static_cast<float *>(p.out) + (static_cast<int64_t>(part) * p.M + m0) * p.N + n0;
+        store_tile_w(root, lds, ws, p.N, p.M - m0, p.N - n0, false);
+    } else if (p.mode == kOutBF16) {
+        store_tile_w(root, lds, static_cast<uint16_t *>(p.out) + m0 * p.N + n0, p.N, p.M - m0,
+                     p.N - n0, true);
+    } else {
+        store_tile_w(root, lds, static_cast<float *>(p.out) + m0 * p.N + n0, p.N, p.M - m0,
+                     p.N - n0, false);
+    }
+}
+
 // Top log2(P) tree levels over the partition roots ws[p][M][N].
 template <int P>
 __global__ __launch_bounds__(256) void partition_combine_kernel(const float *ws, void *out,
@@ -139,14 +171,26 @@ __global__ __launch_bounds__(256) void partition_combine4_kernel(const float *ws
     }
 }
 
-// Trees of at most two leaves per workgroup fit the two-workgroups-per-CU
-// shape, which a grid of more workgroups than CUs fills best; deeper trees,
-// and grids of at most one workgroup per CU, take the eight-wave shape
-// (its deeper ring hides more of the load latency when a CU holds only one
-// workgroup).  Both give the same bits.
+// Workgroups of at most four leaves over at least 16 stages take the
+// 128 x 256 tile when there is at least one such tile per CU (measured at
+// 4096 x 2048 x 2048 with 4 leaves: 44.1 -> 39.7 us; 4096^3 in 4 partitions:
+// 301 -> 255 us; shorter K or fewer tiles ran as fast or slower).  Otherwise
+// trees of at most two leaves fit the two-workgroups-per-CU shape, which a
+// grid of more workgroups than CUs fills best; deeper trees, and grids of at
+// most one workgroup per CU, take the eight-wave shape (its deeper ring
+// hides more of the load latency when a CU holds only one workgroup).  All
+// give the same bits.
 template <int LOG>
 static hipError_t launch_leaf(const GemmParams &p, int parts, hipStream_t stream)
 {
+    if constexpr (LOG <= 2) {
+        const int64_t wide = ((p.N + WBN - 1) / WBN) * ((p.M + BM - 1) / BM);
+        if ((int64_t)p.stages_per_leaf << LOG >= 16 && wide * parts >= device_cus()) {
+            hipLaunchKernelGGL((gemm_wide_kernel<LOG>), dim3(static_cast<unsigned>(wide * parts)),
+                               dim3(256), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     const int64_t tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
     dim3 grid(static_cast<unsigned>(tiles * parts));
     if (LOG <= 1 && tiles * parts > device_cus())

@@ -164,6 +164,37 @@ def test_prefill_full_size():
     assert np.array_equal(bf, f32_to_bf16_bits(C))
 
 
+@pytest.mark.parametrize("M,N,K,L", [(4100, 2100, 2048, 4), (2048, 4000, 2048, 2), (4000, 2304, 1024, 1)])
+def test_wide_tile_ragged(M, N, K, L):
+    """Shapes that take the 128 x 256 tile kernel (at most four leaves per workgroup, at least
+    16 stages, a tile per CU), with ragged M and N: sampled elements (edges and the 256-column
+    tile boundaries included) against the oracle; every element equal across partitions (P = 2
+    also wide, P = 4 and 8 on the 128 x 128 kernels), bf16 output, and the last 70 rows alone
+    (a small batch on other kernels)."""
+    t = torch()
+    A = normal_bf16(M + L, (M, K), 1.0)
+    Wt = normal_bf16(N + L, (N, K), 0.02)
+    c = iso.contract(L, K // L, 0)
+    dA, dW = dev(A), dev(Wt)
+    note(f"wide tile M={M} N={N} K={K} L={L}")
+    C = host(iso.gemm(dA, dW, c))
+    rng = np.random.default_rng(M + N)
+    rows = np.concatenate([[0, M - 1, M - 1, 127, 128, M - 1], rng.integers(0, M, 600)])
+    cols = np.concatenate([[N - 1, 0, 255, 256, 255, N - 1 - (N - 1) % 256], rng.integers(0, N, 600)])
+    check_gemm_tol(C[rows, cols], oracle.gemm_elems(A, Wt, L, rows, cols),
+                   absdot(A, Wt, rows, cols), "wide sampled")
+    for P in (2, 4, 8):
+        if L % P:
+            continue
+        note(f"wide tile P={P}")
+        assert np.array_equal(u32(host(iso.gemm(dA, dW, c, partitions=P))), u32(C)), P
+    note("wide tile bf16 out")
+    assert np.array_equal(host(iso.gemm(dA, dW, c, out_dtype=iso.BF16)), f32_to_bf16_bits(C))
+    note("wide tile last 70 rows alone")
+    tail = host(iso.gemm(dev(A[M - 70:]), dW, c))
+    assert np.array_equal(u32(tail), u32(C[M - 70:]))
+
+
 def test_baseline_accuracy():
     M, N, K = 129, 257, 2048
     A = normal_bf16(9, (M, K), 1.0)
