@@ -40,14 +40,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b)
 }
 
 // float -> bf16 bit pattern, round to nearest, ties to even (finite inputs;
-// NaN stays NaN).
+// infinities stay infinite, NaN stays NaN).  Written as a select rather than
+// a branch, so that kernels converting many values in a row keep straight-
+// line code.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u)
-        return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    // 0x40 (a quiet-NaN bit) when the low half is nonzero, without a compare
+    const uint32_t special = (u >> 16) | ((((u & 0xffffu) + 0xffffu) >> 16) << 6);
+    return static_cast<uint16_t>((u & 0x7f800000u) == 0x7f800000u ? special : rounded);
 }
 
 // e^x for x <= 0 as 2^(x * log2 e) on the hardware exp2 (one rounding of the

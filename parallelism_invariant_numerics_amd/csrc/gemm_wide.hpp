@@ -41,10 +41,12 @@ constexpr int kWLdsBytes = kWBuf * kWStageBytes;       // 144 KiB
 
 // Per-lane ring state: lane l of wave w loads A rows 32 w + 8 i + (l >> 3)
 // (i < 4) and B rows 64 w + 8 i + (l >> 3) (i < 8); voff* are the byte
-// offsets of those rows' swizzled 16-byte chunks.  Rows past a matrix edge
-// have offsets past the buffer range and read as zero.
+// offsets of those rows' swizzled 16-byte chunks.  B row groups i with bit 1
+// set read through rb2 (a second source; the same as rb for one matrix).
+// Rows past a matrix edge have offsets past the buffer range and read as
+// zero.
 struct PipeW {
-    __amdgpu_buffer_rsrc_t ra, rb;
+    __amdgpu_buffer_rsrc_t ra, rb, rb2;
     uint32_t voffa[4];
     uint32_t voffb[8];
     uint32_t kbyte0;  // byte offset of the workgroup's first k
@@ -66,6 +68,7 @@ __device__ __forceinline__ PipeW make_pipe_w(const uint16_t *A_tile, int64_t row
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     p.ra = tile_rsrc(A_tile, rowsA < BM ? rowsA : BM, K);
     p.rb = tile_rsrc(B_tile, rowsB < WBN ? rowsB : WBN, K);
+    p.rb2 = p.rb;
     const uint32_t c = (lane & 7) ^ (lane >> 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -93,7 +96,7 @@ __device__ __forceinline__ void dma_w(const PipeW &p, __amdgpu_buffer_rsrc_t rz,
     char *dst = lds + (st % kWBuf) * kWStageBytes +
                 (q < 4 ? (w * 32 + q * 8) * kRowBytes
                        : kWBOffset + (w * 64 + (q - 4) * 8) * kRowBytes);
-    const __amdgpu_buffer_rsrc_t r = st < nst ? (q < 4 ? p.ra : p.rb) : rz;
+    const __amdgpu_buffer_rsrc_t r = st < nst ? (q < 4 ? p.ra : ((q - 4) & 2) ? p.rb2 : p.rb) : rz;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (ISO_LDS void *)dst, 16,
                                              q < 4 ? p.voffa[q & 3] : p.voffb[(q - 4) & 7], soff,
                                              0, 0);
@@ -241,11 +244,17 @@ __device__ __forceinline__ void stage_w(AccW &acc, FragsW &f0, FragsW &f1, int s
     frags_wait_w(f0);
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t empty_rsrc()
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>((const uint16_t *)nullptr),
+                                             (short)0, 0, 0x00020000);
+}
+
 // The contraction of one 128 x 256 tile over 2^LOG leaves of `spl` stages
 // each.  On return `root` holds the subtree root (wave (wr, wc) holds rows
 // 64 wr + 16 i + 4 (lane >> 4) + r, columns 128 wc + 16 j + (lane & 15) in
-// v[i][j][r]), every ring load has landed and all waves have passed a final
-// barrier, so `lds` may be reused.
+// v[i][j][r]), every load of this wave has landed and all waves have passed
+// a final barrier, so `lds` may be reused.
 template <int LOG>
 __device__ __forceinline__ void leaf_tree_mainloop_w(const PipeW &p, int spl, char *lds,
                                                      AccW &root)
@@ -261,8 +270,7 @@ __device__ __forceinline__ void leaf_tree_mainloop_w(const PipeW &p, int spl, ch
     const uint32_t ch1 = ch0 ^ 64u;
     const uint32_t rowa = (uint32_t)(wr * 64 + (lane & 15)) * kRowBytes;
     const uint32_t rowb = (uint32_t)kWBOffset + (uint32_t)(wc * 128 + (lane & 15)) * kRowBytes;
-    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>((const uint16_t *)nullptr), (short)0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz = empty_rsrc();
 
     for (int s = 0; s < 2; ++s)
         for (int q = 0; q < 12; ++q)

@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "gemm_core.hpp"
+#include "gemm_wide.hpp"
 #include "kernels.h"
 
 namespace iso {
@@ -652,6 +653,168 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(
     }
 }
 
+// ------------------------------------------- gate/up on 128 x 256 tiles
+
+// A wide gate/up task covers 128 intermediate columns n0 .. n0+127.  Its B
+// rows are 16-row blocks that alternate between Wg and Wu: block 2k holds Wg
+// rows n0 + 16k .. n0 + 16k + 15 and block 2k+1 the same Wu rows.  Wave
+// column wc then holds G in its column blocks 2k and U in blocks 2k+1 for
+// the same intermediate columns n0 + 16 (4 wc + k) + (lane & 15), and
+// h = bf16(silu(G) U) is formed in registers (the same device function as
+// every other SwiGLU here).
+constexpr int kGuColsW = 128;
+
+// Ring loads of a wide gate/up task: A rows gathered as in moe_pipe; B group
+// i of wave w is block 4 w + (i >> 1), i.e. Wg for (i & 2) == 0, else Wu.
+__device__ __forceinline__ PipeW moe_gu_pipe_w(const MoeGemmArgs &a, const MoeTask &t,
+                                               const int32_t *rows_s)
+{
+    PipeW p;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t c = (lane & 7) ^ (lane >> 3);
+    p.ra = tile_rsrc(a.A, a.a_rows_total, a.K);
+    const uint32_t oob = (uint32_t)(a.a_rows_total * a.K * 2);
+    int32_t ent[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        lds_issue_b32(ent[i], lds_addr(rows_s + 32 * w + 8 * i + (lane >> 3)));
+    lds_wait();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lds_pin(ent[i]);
+        const int r = 32 * w + 8 * i + (lane >> 3);
+        p.voffa[i] = r < t.nvalid ? (uint32_t)((int64_t)(ent[i] / a.row_div) * a.K * 2) + c * 16
+                                  : oob;
+    }
+    const int64_t boff = static_cast<int64_t>(t.e) * a.N * a.K + t.n0 * a.K;
+    const int64_t brows = a.N - t.n0 < kGuColsW ? a.N - t.n0 : kGuColsW;
+    p.rb = tile_rsrc(a.B0 + boff, brows, a.K);
+    p.rb2 = tile_rsrc(a.B1 + boff, brows, a.K);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t r = (uint32_t)((((4 * w + (i >> 1)) >> 1) << 4) + 8 * (i & 1) + (lane >> 3));
+        p.voffb[i] = (uint32_t)((int64_t)r * a.K * 2) + c * 16;
+    }
+    p.kbyte0 = 0;
+    return p;
+}
+
+// h for the task's rows into `stg` (32 KiB of LDS: 128 rows of 128 bf16;
+// 16-byte chunk q of row r at q ^ (2 ((r >> 2) & 3))), then 16-byte stores of
+// the valid rows to h[rows_s[r]][n0 ..].  LDS accesses are inline assembly
+// (the next task's ring loads are in flight); ends with a barrier.
+__device__ __forceinline__ void moe_gu_epilogue_w(const MoeGemmArgs &a, const MoeTask &t,
+                                                  const AccW &r, const int32_t *rows_s, char *stg)
+{
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave >> 1, wc = wave & 1;
+    const uint32_t sb = lds_addr(stg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t hv = f32_to_bf16_rne(swiglu_act(r.v[i][2 * k][q], r.v[i][2 * k + 1][q]));
+                const int row = wr * 64 + i * 16 + (lane >> 4) * 4 + q;
+                const int col = (4 * wc + k) * 16 + (lane & 15);
+                const int chunk = (col >> 3) ^ (((row >> 2) & 3) << 1);
+                asm volatile("ds_write_b16 %0, %1" ::"v"(sb + row * 256 + chunk * 16 + (col & 7) * 2),
+                             "v"(hv)
+                             : "memory");
+            }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // h through a buffer resource: 32-bit offsets, no 64-bit address registers
+    int64_t hbytes = a.a_rows_total * a.row_div * a.N * 2;
+    if (hbytes > 0xffffffffLL)
+        hbytes = 0xffffffffLL;
+    const __amdgpu_buffer_rsrc_t hr =
+        __builtin_amdgcn_make_buffer_rsrc(a.out, (short)0, (int)(uint32_t)hbytes, 0x00020000);
+    const bool al = (reinterpret_cast<uintptr_t>(a.out) % 16 == 0) && (a.N % 8 == 0) &&
+                    (t.n0 % 8 == 0);
+    const int cmax = a.N - t.n0 < kGuColsW ? static_cast<int>(a.N - t.n0) : kGuColsW;
+    constexpr int UPT = BM * (kGuColsW / 8) / 256;  // 16-byte units per thread
+    // the thread index through lane_id(): addresses derived from it are not
+    // hoisted out of the task loop (where they would only be spilled)
+    const int tid = wave * 64 + lane;
+    u32x4 v[UPT];
+    int32_t dst[UPT];
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        const int u = tid + k * 256;
+        const int row = u >> 4, q = u & 15;
+        asm volatile("ds_read_b128 %0, %1"
+                     : "=v"(v[k])
+                     : "v"(sb + row * 256 + ((q ^ (((row >> 2) & 3) << 1)) << 4)));
+        lds_issue_b32(dst[k], lds_addr(rows_s + row));
+    }
+    lds_wait();
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+        lds_pin(v[k]);
+        lds_pin(dst[k]);
+        const int u = tid + k * 256;
+        const int row = u >> 4, q = u & 15;
+        if (row >= t.nvalid)
+            continue;
+        const uint32_t off = (uint32_t)((dst[k] * a.N + t.n0 + 8 * q) * 2);
+        if (al && 8 * q + 8 <= cmax) {
+            __builtin_amdgcn_raw_buffer_store_b128(v[k], hr, off, 0, 0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e < cmax - 8 * q)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        static_cast<uint16_t>(v[k][e >> 1] >> (16 * (e & 1))), hr, off + 2 * e, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_barrier();
+}
+
+// Persistent over the wide gate/up tasks, one workgroup per CU, with the
+// XCD-aware task split of moe_expert_kernel.  The next task's bucket entries
+// are fetched during the main loop; the epilogue stages h through the third
+// ring slot.  (Requesting the next task's first ring stages before the
+// epilogue measured no faster, and a register reload in the epilogue would
+// then wait for those loads.)
+template <int LOG>
+__global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
+                                                             const int32_t *__restrict__ tiles,
+                                                             const int32_t *__restrict__ counts,
+                                                             const int32_t *__restrict__ ntiles)
+{
+    __shared__ __attribute__((aligned(16))) char lds[kWLdsBytes];
+    __shared__ int32_t rows_s[2][BM];
+    char *stg = lds + 2 * kWStageBytes;
+    const int ntn = static_cast<int>((a.N + kGuColsW - 1) / kGuColsW);
+    const int total = __builtin_amdgcn_readfirstlane(*ntiles) * ntn;
+    const int xcd = blockIdx.x % kXcds;
+    const int slots = gridDim.x / kXcds;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int end = (xcd + 1) * per < total ? (xcd + 1) * per : total;
+    int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds;
+    if (w >= end)
+        return;
+    rows_dma(a, moe_task(tiles, counts, w, ntn, kGuColsW), rows_s[0]);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int it = 0;; ++it) {
+        const int b = it & 1;
+        const MoeTask t = moe_task(tiles, counts, w, ntn, kGuColsW);
+        const int wn = w + slots;
+        const PipeW p = moe_gu_pipe_w(a, t, rows_s[b]);
+        if (wn < end)
+            rows_dma(a, moe_task(tiles, counts, wn, ntn, kGuColsW), rows_s[b ^ 1]);
+        AccW r0;
+        leaf_tree_mainloop_w<LOG>(p, a.stages_per_leaf, lds, r0);
+        moe_gu_epilogue_w(a, t, r0, rows_s[b], stg);
+        if (wn >= end)
+            break;
+        w = wn;
+    }
+}
+
 // --------------------------------------------------------------- combine
 
 // y[t][n] = g_0 e_0 + g_1 e_1 + ... in routing order, left to right, each
@@ -692,9 +855,28 @@ static void launch_expert(const MoeGemmArgs &a, hipStream_t stream)
                        a, a.tiles, a.counts, a.ntiles);
 }
 
+// Gate/up with at most four leaves over at least 16 stages takes the
+// 128 x 256 tile; same bits as the 128 x 128 expert kernel.
+template <int LOG>
+static void launch_gu_wide(const MoeGemmArgs &a, hipStream_t stream)
+{
+    const unsigned grid = static_cast<unsigned>(device_cus() / kXcds * kXcds);
+    hipLaunchKernelGGL((moe_gu_wide_kernel<LOG>), dim3(grid), dim3(256), 0, stream, a, a.tiles,
+                       a.counts, a.ntiles);
+}
+
 template <bool GU>
 static hipError_t dispatch_expert(const MoeGemmArgs &a, int leaves, hipStream_t stream)
 {
+    if (GU && leaves <= 4 && a.stages_per_leaf * leaves >= 16) {
+        switch (leaves) {
+        case 1: launch_gu_wide<0>(a, stream); break;
+        case 2: launch_gu_wide<1>(a, stream); break;
+        case 4: launch_gu_wide<2>(a, stream); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (leaves) {
     case 1: launch_expert<0, GU>(a, stream); break;
     case 2: launch_expert<1, GU>(a, stream); break;
