@@ -157,6 +157,7 @@ def _source_hash(files):
 
 
 GEMM_SOURCES = ["parallelism_invariant_numerics_amd/csrc/gemm_core.hpp",
+                "parallelism_invariant_numerics_amd/csrc/gemm_wide.hpp",
                 "parallelism_invariant_numerics_amd/csrc/gemm.hip",
                 "parallelism_invariant_numerics_amd/csrc/device_common.hpp"]
 
