@@ -193,12 +193,15 @@ static hipError_t launch_leaf(const GemmParams &p, int parts, hipStream_t stream
     }
     const int64_t tiles = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
     dim3 grid(static_cast<unsigned>(tiles * parts));
-    if (LOG <= 1 && tiles * parts > device_cus())
-        hipLaunchKernelGGL((gemm_leaf_kernel<CfgDual, LOG>), grid, dim3(CfgDual::kThreads), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((gemm_leaf_kernel<CfgWide, LOG>), grid, dim3(CfgWide::kThreads), 0,
-                           stream, p);
+    if constexpr (LOG <= 1) {
+        if (tiles * parts > device_cus()) {
+            hipLaunchKernelGGL((gemm_leaf_kernel<CfgDual, LOG>), grid, dim3(CfgDual::kThreads), 0,
+                               stream, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_leaf_kernel<CfgWide, LOG>), grid, dim3(CfgWide::kThreads), 0, stream,
+                       p);
     return hipGetLastError();
 }
 
