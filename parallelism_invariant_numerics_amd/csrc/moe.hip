@@ -815,6 +815,325 @@ __global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
     }
 }
 
+// ------------------------------- down projection with the rows in registers
+
+// A down task: an expert's 128-row tile times up to kDnCT column tiles of
+// 128 output columns.  The task's rows of h (K = I = 32 KS) are loaded once
+// into AGPRs; the Wd rows stream through a ring of four 16 KiB LDS stages
+// (128 rows x 64 k, chunk-swizzled as in gemm_core.hpp), one column tile
+// after another without draining.  The MFMA takes the weights as its first
+// operand and the rows as its second: every output element is still the
+// same products summed in the same k order from +0.0 (the same leaves and
+// tree as every other kernel), and a lane's four accumulator values are
+// four consecutive output columns of one row, which leave as one 16-byte
+// store straight from registers.  Four waves, one per SIMD: wave (wr, wc)
+// holds rows 64 wr .. 64 wr + 63 and columns 64 wc .. 64 wc + 63 of the
+// column tile.
+constexpr int kDnCT = 4;
+constexpr int kDnStage = 128 * kRowBytes;  // 16 KiB
+constexpr int kDnBuf = 4;
+
+template <int KS>
+struct DnRows {
+    bf16x8 v[4][KS];  // row block i, k-step
+};
+struct DnAcc {
+    f32x4 v[4][4];  // row block i, column block j
+};
+struct DnFrags {
+    bf16x8 b[4];
+};
+
+// acc (+)= Wd block j x rows block i (the transposed product; see above).
+template <bool FRESH>
+__device__ __forceinline__ void mfma_dn(f32x4 &acc, const bf16x8 &w, const bf16x8 &r)
+{
+    if constexpr (FRESH)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(w), "a"(r));
+    else
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(w), "a"(r));
+}
+
+template <int J>
+__device__ __forceinline__ void dn_frag(DnFrags &f, uint32_t addr)
+{
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(f.b[J]) : "v"(addr), "i"(J * 16 * kRowBytes));
+}
+
+__device__ __forceinline__ void dn_frags_wait(DnFrags &f)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        asm volatile("" : "+v"(f.b[j]));
+}
+
+// The 4 ring loads of global stage g of the task (column tile g / spt,
+// k stage g % spt) for this wave: Wd rows 32 w + 8 q + (lane >> 3) of the
+// column tile.
+__device__ __forceinline__ void dn_dma(__amdgpu_buffer_rsrc_t rb, const uint32_t (&voff)[4],
+                                       char *lds, int g, int spt, int64_t K)
+{
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = g / spt, st = g - c * spt;
+    const uint32_t soff = (uint32_t)(c * 128 * K * 2) + (uint32_t)st * (BK * 2);
+    char *dst = lds + (g % kDnBuf) * kDnStage + w * 32 * kRowBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ISO_LDS void *)(dst + q * 8 * kRowBytes), 16,
+                                                 voff[q], soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) for n in {0, 4, 8}, then a workgroup barrier.
+__device__ __forceinline__ void dn_vm_barrier(int n)
+{
+    if (n >= 8)
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else if (n >= 4)
+        asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void dn_drain(DnAcc &acc)
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            asm volatile("" : "+v"(acc.v[i][j]));
+}
+
+// Tree level 1 (the sum of two leaves, saved while the next two run) of a
+// four-leaf tree is kept in LDS, each wave in its own 16 KiB (the rows take
+// the AGPRs, and three register sets of 64 do not fit beside them); the
+// values pass unchanged.  `l1` is this lane's address in that region.
+__device__ __forceinline__ void dn_park_lds(const DnAcc &v, uint32_t l1)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(l1), "v"(v.v[i][j]),
+                         "i"((i * 4 + j) * 1024)
+                         : "memory");
+}
+
+__device__ __forceinline__ void dn_unpark_lds(DnAcc &left, uint32_t l1)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            asm volatile("ds_read_b128 %0, %1 offset:%2"
+                         : "=v"(left.v[i][j])
+                         : "v"(l1), "i"((i * 4 + j) * 1024));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            asm volatile("" : "+v"(left.v[i][j]));
+}
+
+template <int LOG, int J, int B>
+__device__ __forceinline__ void dn_tree_push(DnAcc (&stk)[LOG > 0 ? LOG : 1], DnAcc &v, uint32_t l1)
+{
+    constexpr bool IN_LDS = LOG == 2 && B == 1;
+    if constexpr (B < LOG) {
+        if constexpr (((J >> B) & 1) != 0) {
+            if constexpr (IN_LDS)
+                dn_unpark_lds(stk[B], l1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v.v[i][j] = stk[B].v[i][j] + v.v[i][j];
+            dn_tree_push<LOG, J, B + 1>(stk, v, l1);
+        } else {
+            if constexpr (IN_LDS)
+                dn_park_lds(v, l1);
+            else
+                stk[B] = v;
+        }
+    }
+}
+
+// One k-step: 16 MFMAs on the fragments f and row k-step KSI, with the four
+// reads of fn (address fa, when RD) after the first four MFMAs and the four
+// ring loads of stage dg (when DM) after the next four.
+template <int KS, int KSI, bool FRESH, bool RD>
+__device__ __forceinline__ void dn_kstep(DnAcc &acc, const DnRows<KS> &rows, const DnFrags &f,
+                                         DnFrags &fn, uint32_t fa, bool dm,
+                                         __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff)[4],
+                                         char *lds, int dg, int spt, int64_t K)
+{
+    static_for<16>([&](auto Mc) {
+        constexpr int m = decltype(Mc)::value;
+        constexpr int i = m / 4, j = m % 4;
+        mfma_dn<FRESH>(acc.v[i][j], f.b[j], rows.v[i][KSI]);
+        if constexpr (RD && m < 4)
+            dn_frag<m>(fn, fa);
+        if constexpr (m == 7) {
+            if (dm)
+                dn_dma(rb, voff, lds, dg, spt, K);
+        }
+    });
+}
+
+// Stages of one column tile c (ring stages g0 .. g0 + KS/2 - 1 of the task,
+// `total` in all); on entry f0 holds the first k-step's fragments.  Loads of
+// stage t are issued in the second k-step of stage t - 4 (the first four in
+// the prologue), so at the barrier after the first k-step of stage g only
+// the loads of stages g + 2 and g + 3 were issued after those of stage g + 1.
+template <int KS, int LOG, int S>
+__device__ __forceinline__ void dn_stages(DnAcc &acc, DnAcc (&stk)[LOG > 0 ? LOG : 1],
+                                          const DnRows<KS> &rows, DnFrags &f0, DnFrags &f1,
+                                          int g0, int total, uint32_t lds_base, uint32_t rowb,
+                                          uint32_t ch0, uint32_t ch1,
+                                          __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff)[4],
+                                          char *lds, int64_t K, uint32_t l1)
+{
+    constexpr int SPT = KS / 2;
+    constexpr int LK = KS >> LOG;  // k-steps per leaf
+    if constexpr (S < SPT) {
+        const int g = g0 + S;
+        const uint32_t bs = lds_base + (uint32_t)(g % kDnBuf) * kDnStage + rowb;
+        dn_kstep<KS, 2 * S, (2 * S) % LK == 0, true>(acc, rows, f0, f1, bs + ch1, false, rb, voff,
+                                                      lds, 0, SPT, K);
+        dn_frags_wait(f1);
+        const int pend = (g + 2 < total ? 4 : 0) + (g + 3 < total ? 4 : 0);
+        dn_vm_barrier(pend);
+        const uint32_t bn = lds_base + (uint32_t)((g + 1) % kDnBuf) * kDnStage + rowb;
+        dn_kstep<KS, 2 * S + 1, false, true>(acc, rows, f1, f0, bn + ch0, g + 4 < total, rb, voff,
+                                             lds, g + 4, SPT, K);
+        dn_frags_wait(f0);
+        if constexpr ((2 * S + 2) % LK == 0) {
+            constexpr int J = (2 * S + 2) / LK - 1;  // the leaf just finished
+            dn_drain(acc);
+            dn_tree_push<LOG, J, 0>(stk, acc, l1);
+        }
+        dn_stages<KS, LOG, S + 1>(acc, stk, rows, f0, f1, g0, total, lds_base, rowb, ch0, ch1, rb,
+                                  voff, lds, K, l1);
+    }
+}
+
+// Persistent over the down tasks (the XCD-aware split of moe_expert_kernel),
+// one workgroup of four waves per CU.
+template <int KS, int LOG>
+__global__ __launch_bounds__(256, 1) void moe_down_reg_kernel(MoeGemmArgs a,
+                                                              const int32_t *__restrict__ tiles,
+                                                              const int32_t *__restrict__ counts,
+                                                              const int32_t *__restrict__ ntiles)
+{
+    static_assert((KS >> LOG) >= 2, "a leaf spans at least one ring stage");
+    constexpr int SPT = KS / 2;
+    constexpr int TN = 128 * kDnCT;
+    __shared__ __attribute__((aligned(16))) char lds[kDnBuf * kDnStage + (LOG == 2 ? 4 * 16384 : 0)];
+    const int ntn = static_cast<int>((a.N + TN - 1) / TN);
+    const int total_tasks = __builtin_amdgcn_readfirstlane(*ntiles) * ntn;
+    const int xcd = blockIdx.x % kXcds;
+    const int slots = gridDim.x / kXcds;
+    const int per = (total_tasks + kXcds - 1) / kXcds;
+    const int end = (xcd + 1) * per < total_tasks ? (xcd + 1) * per : total_tasks;
+    const int64_t K = a.K;
+    const uint32_t lds_base = lds_addr(lds);
+    int64_t abytes = a.a_rows_total * K * 2;
+    if (abytes > 0xffffffffLL)
+        abytes = 0xffffffffLL;
+    int64_t ebytes = a.a_rows_total * a.N * 4;
+    if (ebytes > 0xffffffffLL)
+        ebytes = 0xffffffffLL;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.A), (short)0, (int)(uint32_t)abytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t re =
+        __builtin_amdgcn_make_buffer_rsrc(a.out, (short)0, (int)(uint32_t)ebytes, 0x00020000);
+    for (int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds; w < end; w += slots) {
+        const MoeTask t = moe_task(tiles, counts, w, ntn, TN);
+        const int nct = static_cast<int>((a.N - t.n0 + 127) / 128) < kDnCT
+                            ? static_cast<int>((a.N - t.n0 + 127) / 128)
+                            : kDnCT;
+        const int total = nct * SPT;
+        const int lane = lane_id();
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int wr = wave >> 1, wc = wave & 1;
+        // this lane's four rows (one per row block) and their entries
+        int32_t ent[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wr * 64 + i * 16 + (lane & 15);
+            ent[i] = r < t.nvalid ? a.rows[static_cast<int64_t>(t.e) * a.T + t.m0 + r] : -1;
+        }
+        // the Wd rows of the task's column tiles
+        const int64_t boff = static_cast<int64_t>(t.e) * a.N * K + t.n0 * K;
+        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(a.B0 + boff, (int64_t)nct * 128, K);
+        uint32_t voff[4];
+        {
+            const uint32_t c = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                voff[q] = (uint32_t)((int64_t)(32 * wave + 8 * q + (lane >> 3)) * K * 2) + c * 16;
+        }
+        for (int g = 0; g < 4; ++g)
+            if (g < total)
+                dn_dma(rb, voff, lds, g, SPT, K);
+        // the rows, once (past the bucket: an offset past the range reads zero)
+        DnRows<KS> rows;
+        {
+            const uint32_t oob = (uint32_t)abytes;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t base =
+                    ent[i] >= 0 ? (uint32_t)((int64_t)ent[i] * K * 2) + (uint32_t)((lane >> 4) * 16)
+                                : oob;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, base + ks * 64, 0, 0);
+                    rows.v[i][ks] = reinterpret_cast<const bf16x8 &>(v);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    asm volatile("" : "+a"(rows.v[i][ks]));
+        }
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        const uint32_t ch0 = (uint32_t)(((lane >> 4) ^ (lane & 7)) << 4);
+        const uint32_t ch1 = ch0 ^ 64u;
+        const uint32_t rowb = (uint32_t)(wc * 64 + (lane & 15)) * kRowBytes;
+        const uint32_t l1 = lds_base + kDnBuf * kDnStage + wave * 16384 + lane * 16;
+        DnFrags f0, f1;
+        dn_frag<0>(f0, lds_base + rowb + ch0);
+        dn_frag<1>(f0, lds_base + rowb + ch0);
+        dn_frag<2>(f0, lds_base + rowb + ch0);
+        dn_frag<3>(f0, lds_base + rowb + ch0);
+        dn_frags_wait(f0);
+        // output offsets: row ent[i], columns n0 + 128 c + 64 wc + 4 (lane >> 4) + 16 j
+        uint32_t eoff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            eoff[i] = ent[i] >= 0 ? (uint32_t)((int64_t)ent[i] * a.N * 4) +
+                                        (uint32_t)((wc * 64 + 4 * (lane >> 4)) * 4)
+                                  : (uint32_t)ebytes;
+        for (int c = 0; c < nct; ++c) {
+            DnAcc stk[LOG > 0 ? LOG : 1];
+            DnAcc acc;
+            dn_stages<KS, LOG, 0>(acc, stk, rows, f0, f1, c * SPT, total, lds_base, rowb, ch0,
+                                  ch1, rb, voff, lds, K, l1);
+            const uint32_t soff = (uint32_t)((t.n0 + 128 * c) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        reinterpret_cast<const u32x4 &>(acc.v[i][j]), re, eoff[i] + j * 64, soff, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+}
+
 // --------------------------------------------------------------- combine
 
 // y[t][n] = g_0 e_0 + g_1 e_1 + ... in routing order, left to right, each
@@ -888,6 +1207,39 @@ static hipError_t dispatch_expert(const MoeGemmArgs &a, int leaves, hipStream_t 
     return hipGetLastError();
 }
 
+template <int KS, int LOG>
+static void launch_down_reg(const MoeGemmArgs &a, hipStream_t stream)
+{
+    const unsigned grid = static_cast<unsigned>(device_cus() / kXcds * kXcds);
+    hipLaunchKernelGGL((moe_down_reg_kernel<KS, LOG>), dim3(grid), dim3(256), 0, stream, a, a.tiles,
+                       a.counts, a.ntiles);
+}
+
+// The down projection keeps a task's rows in registers when they fit
+// (K = 128, 256 or 512), whole column tiles of 128 cover the output (H a
+// multiple of 128) and a leaf spans at least one ring stage; otherwise the
+// tile kernel.  Same bits either way.
+static hipError_t dispatch_down(const MoeGemmArgs &a, int leaves, hipStream_t stream)
+{
+    const int KS = static_cast<int>(a.K / 32);
+    const bool fits = (a.K == 128 || a.K == 256 || a.K == 512) && a.N % 128 == 0 &&
+                      (leaves == 1 || leaves == 2 || leaves == 4) && KS / leaves >= 2;
+    if (!fits)
+        return dispatch_expert<false>(a, leaves, stream);
+    switch (KS * 8 + leaves) {
+    case 4 * 8 + 1: launch_down_reg<4, 0>(a, stream); break;
+    case 4 * 8 + 2: launch_down_reg<4, 1>(a, stream); break;
+    case 8 * 8 + 1: launch_down_reg<8, 0>(a, stream); break;
+    case 8 * 8 + 2: launch_down_reg<8, 1>(a, stream); break;
+    case 8 * 8 + 4: launch_down_reg<8, 2>(a, stream); break;
+    case 16 * 8 + 1: launch_down_reg<16, 0>(a, stream); break;
+    case 16 * 8 + 2: launch_down_reg<16, 1>(a, stream); break;
+    case 16 * 8 + 4: launch_down_reg<16, 2>(a, stream); break;
+    default: return dispatch_expert<false>(a, leaves, stream);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg,
                       const uint16_t *Wu, const uint16_t *Wd, float *Y, int64_t T, int64_t H,
                       int64_t E, int64_t I, int top_k, int gu_leaves, int gu_leaf_size,
@@ -948,7 +1300,7 @@ hipError_t launch_moe(const uint16_t *X, const float *logits, const uint16_t *Wg
     a.N = H;
     a.K = I;
     a.stages_per_leaf = dn_leaf_size / BK;
-    if ((err = dispatch_expert<false>(a, dn_leaves, stream)) != hipSuccess)
+    if ((err = dispatch_down(a, dn_leaves, stream)) != hipSuccess)
         return err;
     const int64_t quads = T * (H / 4);
     int64_t blocks = (quads + 255) / 256;
