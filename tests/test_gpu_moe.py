@@ -106,11 +106,14 @@ def _check_stages(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, y, st, what):
                                                (50, 1024, 8, 256, 4, 8, 4), (20, 2048, 4, 512, 2, 16, 8),
                                                (300, 2048, 16, 512, 8, 4, 4),
                                                (90, 1024, 8, 192, 4, 4, 1), (70, 2048, 8, 320, 2, 2, 1),
-                                               (40, 1024, 4, 128, 2, 1, 1)])
+                                               (40, 1024, 4, 128, 2, 1, 1), (33, 1024, 8, 512, 2, 4, 2),
+                                               (45, 512, 4, 512, 4, 2, 1), (25, 192, 4, 128, 2, 1, 2)])
 def test_small_parity_by_stage(T, H, E, I, k, Lgu, Ldn):
     """Every stage against the oracle.  Gate/up with at most four leaves over 16 or more
-    stages of K (H = 1024, 2048 here) runs on 128 x 256 tiles, the rest on 128 x 128; the
-    last three cases give it a ragged intermediate size and 2 and 1 leaves."""
+    stages of K (H = 1024, 2048 here) runs on 128 x 256 tiles, the rest on 128 x 128 (three
+    cases give it a ragged intermediate size and 2 and 1 leaves).  The down projection keeps
+    its rows in registers for I = 128, 256, 512 with 1, 2 or 4 leaves and H a multiple of 128
+    (every case here but I = 64, 192, 320, 8 leaves, and H = 192)."""
     X = normal_bf16(T + 1, (T, H), 1.0)
     lg = normal_f32(T + 2, (T, E))
     Wg = normal_bf16(T + 3, (E, I, H), 0.05)
