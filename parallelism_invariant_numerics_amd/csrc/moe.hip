@@ -818,33 +818,32 @@ __global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
 // ------------------------------- down projection with the rows in registers
 
 // A down task: an expert's 128-row tile times up to kDnCT column tiles of
-// 128 output columns.  The task's rows of h (K = I = 32 KS) are loaded once
-// into AGPRs; the Wd rows stream through a ring of four 16 KiB LDS stages
-// (128 rows x 64 k, chunk-swizzled as in gemm_core.hpp), one column tile
-// after another without draining.  The MFMA takes the weights as its first
-// operand and the rows as its second: every output element is still the
-// same products summed in the same k order from +0.0 (the same leaves and
-// tree as every other kernel), and a lane's four accumulator values are
-// four consecutive output columns of one row, which leave as one 16-byte
-// store straight from registers.  Four waves, one per SIMD: wave (wr, wc)
-// holds rows 64 wr .. 64 wr + 63 and columns 64 wc .. 64 wc + 63 of the
-// column tile.
+// 128 output columns.  Each of the four waves (one per SIMD) holds 32 of the
+// task's rows of h (K = I = 32 KS) in AGPRs, for all the task's column
+// tiles (each wave loads only its own rows); the Wd rows stream through a
+// ring of four 16 KiB LDS stages (128 rows x 64 k, chunk-swizzled as in
+// gemm_core.hpp), one column tile after another without draining.  The MFMA
+// takes the weights as its first operand and the rows as its second: every output element is
+// still the same products summed in the same k order from +0.0 (the same
+// leaves and tree as every other kernel), and a lane's four accumulator
+// values are four consecutive output columns of one row, which leave as one
+// 16-byte store straight from registers.
 constexpr int kDnCT = 4;
 constexpr int kDnStage = 128 * kRowBytes;  // 16 KiB
 constexpr int kDnBuf = 4;
 
 template <int KS>
 struct DnRows {
-    bf16x8 v[4][KS];  // row block i, k-step
+    bf16x8 v[2][KS];  // row block i (16 rows), k-step
 };
 struct DnAcc {
-    f32x4 v[4][4];  // row block i, column block j
+    f32x4 v[2][8];  // row block i, column block j
 };
 struct DnFrags {
-    bf16x8 b[4];
+    bf16x8 b[8];  // column blocks of one k-step
 };
 
-// acc (+)= Wd block j x rows block i (the transposed product; see above).
+// acc (+)= Wd block x rows block (the transposed product; see above).
 template <bool FRESH>
 __device__ __forceinline__ void mfma_dn(f32x4 &acc, const bf16x8 &w, const bf16x8 &r)
 {
@@ -864,76 +863,84 @@ __device__ __forceinline__ void dn_frags_wait(DnFrags &f)
 {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
         asm volatile("" : "+v"(f.b[j]));
 }
 
-// The 4 ring loads of global stage g of the task (column tile g / spt,
-// k stage g % spt) for this wave: Wd rows 32 w + 8 q + (lane >> 3) of the
-// column tile.
+// Ring load q of global stage g of the task (column tile g / spt, k stage
+// g % spt) for this wave: Wd rows 32 w + 8 q + (lane >> 3) of the tile.
 __device__ __forceinline__ void dn_dma(__amdgpu_buffer_rsrc_t rb, const uint32_t (&voff)[4],
-                                       char *lds, int g, int spt, int64_t K)
+                                       char *lds, int g, int spt, int64_t K, int q)
 {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = g / spt, st = g - c * spt;
     const uint32_t soff = (uint32_t)(c * 128 * K * 2) + (uint32_t)st * (BK * 2);
-    char *dst = lds + (g % kDnBuf) * kDnStage + w * 32 * kRowBytes;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ISO_LDS void *)(dst + q * 8 * kRowBytes), 16,
-                                                 voff[q], soff, 0, 0);
+    char *dst = lds + (g % kDnBuf) * kDnStage + (w * 32 + q * 8) * kRowBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ISO_LDS void *)dst, 16, voff[q], soff, 0, 0);
 }
 
-// s_waitcnt vmcnt(n) for n in {0, 4, 8}, then a workgroup barrier.
+// Rows of a task: this lane's 16-byte piece of k-step ks of row block i
+// (row 32 w + 16 i + (lane & 15), k 32 ks + 8 (lane >> 4) ..), read through
+// `ra` at byte offset base[i] + 64 ks (past the range: zeros).
+template <int KS>
+__device__ __forceinline__ void dn_row_load(DnRows<KS> &rows, __amdgpu_buffer_rsrc_t ra,
+                                            const uint32_t (&base)[2], int i, int ks)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, base[i] + ks * 64, 0, 0);
+    rows.v[i][ks] = reinterpret_cast<const bf16x8 &>(v);
+}
+
+// s_waitcnt vmcnt(n) for n in {0, 4, 8, 12}, then a workgroup barrier.
+// Later stores only make the wait stricter.
 __device__ __forceinline__ void dn_vm_barrier(int n)
 {
-    if (n >= 8)
-        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-    else if (n >= 4)
-        asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    switch (n) {
+    case 12: asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    }
 }
 
 __device__ __forceinline__ void dn_drain(DnAcc &acc)
 {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
             asm volatile("" : "+v"(acc.v[i][j]));
 }
 
 // Tree level 1 (the sum of two leaves, saved while the next two run) of a
-// four-leaf tree is kept in LDS, each wave in its own 16 KiB (the rows take
-// the AGPRs, and three register sets of 64 do not fit beside them); the
-// values pass unchanged.  `l1` is this lane's address in that region.
+// four-leaf tree is kept in LDS, each wave in its own 16 KiB (three register
+// sets of 64 do not fit beside the rows and fragments); the values pass
+// unchanged.  `l1` is this lane's address in that region.
 __device__ __forceinline__ void dn_park_lds(const DnAcc &v, uint32_t l1)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
             asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(l1), "v"(v.v[i][j]),
-                         "i"((i * 4 + j) * 1024)
+                         "i"((i * 8 + j) * 1024)
                          : "memory");
 }
 
 __device__ __forceinline__ void dn_unpark_lds(DnAcc &left, uint32_t l1)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
             asm volatile("ds_read_b128 %0, %1 offset:%2"
                          : "=v"(left.v[i][j])
-                         : "v"(l1), "i"((i * 4 + j) * 1024));
+                         : "v"(l1), "i"((i * 8 + j) * 1024));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
             asm volatile("" : "+v"(left.v[i][j]));
 }
 
@@ -946,9 +953,9 @@ __device__ __forceinline__ void dn_tree_push(DnAcc (&stk)[LOG > 0 ? LOG : 1], Dn
             if constexpr (IN_LDS)
                 dn_unpark_lds(stk[B], l1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 8; ++j)
                     v.v[i][j] = stk[B].v[i][j] + v.v[i][j];
             dn_tree_push<LOG, J, B + 1>(stk, v, l1);
         } else {
@@ -960,63 +967,149 @@ __device__ __forceinline__ void dn_tree_push(DnAcc (&stk)[LOG > 0 ? LOG : 1], Dn
     }
 }
 
-// One k-step: 16 MFMAs on the fragments f and row k-step KSI, with the four
-// reads of fn (address fa, when RD) after the first four MFMAs and the four
-// ring loads of stage dg (when DM) after the next four.
+// What one task needs besides its rows.
+struct DnTask {
+    int nct, total;                  // column tiles, ring stages
+    int64_t n0;                      // first output column
+    __amdgpu_buffer_rsrc_t rb;       // the Wd rows of its column tiles
+    uint32_t eoff[2];                // output byte offsets of this lane's two rows
+};
+
+// Per-call constants of the kernel.
+struct DnCtx {
+    __amdgpu_buffer_rsrc_t ra, re;   // h rows, e
+    uint32_t voff[4];                // ring load offsets of this lane
+    uint32_t lds_base, rowb, ch0, ch1, l1;
+    char *lds;
+    int64_t K;
+};
+
+// One k-step: 16 MFMAs on the fragments f and row k-step KSI; after MFMA m
+// the fragment read m of fn (m < 8, when RD) and ring load m - 8 of stage
+// dg (8 <= m < 12, when dm).
 template <int KS, int KSI, bool FRESH, bool RD>
 __device__ __forceinline__ void dn_kstep(DnAcc &acc, const DnRows<KS> &rows, const DnFrags &f,
-                                         DnFrags &fn, uint32_t fa, bool dm,
-                                         __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff)[4],
-                                         char *lds, int dg, int spt, int64_t K)
+                                         DnFrags &fn, uint32_t fa, bool dm, int dg,
+                                         const DnTask &t, const DnCtx &x)
 {
     static_for<16>([&](auto Mc) {
         constexpr int m = decltype(Mc)::value;
-        constexpr int i = m / 4, j = m % 4;
+        constexpr int i = m / 8, j = m % 8;
         mfma_dn<FRESH>(acc.v[i][j], f.b[j], rows.v[i][KSI]);
-        if constexpr (RD && m < 4)
+        if constexpr (RD && m < 8)
             dn_frag<m>(fn, fa);
-        if constexpr (m == 7) {
+        if constexpr (m >= 8 && m < 12) {
             if (dm)
-                dn_dma(rb, voff, lds, dg, spt, K);
+                dn_dma(t.rb, x.voff, x.lds, dg, KS / 2, x.K, m - 8);
         }
     });
 }
 
-// Stages of one column tile c (ring stages g0 .. g0 + KS/2 - 1 of the task,
-// `total` in all); on entry f0 holds the first k-step's fragments.  Loads of
-// stage t are issued in the second k-step of stage t - 4 (the first four in
-// the prologue), so at the barrier after the first k-step of stage g only
-// the loads of stages g + 2 and g + 3 were issued after those of stage g + 1.
+// Stages of column tile c (ring stages g0 .. g0 + KS/2 - 1 of the task);
+// on entry f0 holds the first k-step's fragments.  Loads of stage t are
+// issued in the second k-step of stage t - 4 (the first four in the
+// prologue), so at the barrier after the first k-step of stage g only the
+// loads of stages g + 2 and g + 3 were issued after those of stage g + 1.
 template <int KS, int LOG, int S>
 __device__ __forceinline__ void dn_stages(DnAcc &acc, DnAcc (&stk)[LOG > 0 ? LOG : 1],
                                           const DnRows<KS> &rows, DnFrags &f0, DnFrags &f1,
-                                          int g0, int total, uint32_t lds_base, uint32_t rowb,
-                                          uint32_t ch0, uint32_t ch1,
-                                          __amdgpu_buffer_rsrc_t rb, const uint32_t (&voff)[4],
-                                          char *lds, int64_t K, uint32_t l1)
+                                          int g0, const DnTask &t, const DnCtx &x)
 {
     constexpr int SPT = KS / 2;
     constexpr int LK = KS >> LOG;  // k-steps per leaf
     if constexpr (S < SPT) {
         const int g = g0 + S;
-        const uint32_t bs = lds_base + (uint32_t)(g % kDnBuf) * kDnStage + rowb;
-        dn_kstep<KS, 2 * S, (2 * S) % LK == 0, true>(acc, rows, f0, f1, bs + ch1, false, rb, voff,
-                                                      lds, 0, SPT, K);
+        const uint32_t bs = x.lds_base + (uint32_t)(g % kDnBuf) * kDnStage + x.rowb;
+        dn_kstep<KS, 2 * S, (2 * S) % LK == 0, true>(acc, rows, f0, f1, bs + x.ch1, false, 0, t, x);
         dn_frags_wait(f1);
-        const int pend = (g + 2 < total ? 4 : 0) + (g + 3 < total ? 4 : 0);
-        dn_vm_barrier(pend);
-        const uint32_t bn = lds_base + (uint32_t)((g + 1) % kDnBuf) * kDnStage + rowb;
-        dn_kstep<KS, 2 * S + 1, false, true>(acc, rows, f1, f0, bn + ch0, g + 4 < total, rb, voff,
-                                             lds, g + 4, SPT, K);
+        dn_vm_barrier((g + 2 < t.total ? 4 : 0) + (g + 3 < t.total ? 4 : 0));
+        const uint32_t bn = x.lds_base + (uint32_t)((g + 1) % kDnBuf) * kDnStage + x.rowb;
+        dn_kstep<KS, 2 * S + 1, false, true>(acc, rows, f1, f0, bn + x.ch0, g + 4 < t.total, g + 4,
+                                             t, x);
         dn_frags_wait(f0);
         if constexpr ((2 * S + 2) % LK == 0) {
             constexpr int J = (2 * S + 2) / LK - 1;  // the leaf just finished
             dn_drain(acc);
-            dn_tree_push<LOG, J, 0>(stk, acc, l1);
+            dn_tree_push<LOG, J, 0>(stk, acc, x.l1);
         }
-        dn_stages<KS, LOG, S + 1>(acc, stk, rows, f0, f1, g0, total, lds_base, rowb, ch0, ch1, rb,
-                                  voff, lds, K, l1);
+        dn_stages<KS, LOG, S + 1>(acc, stk, rows, f0, f1, g0, t, x);
     }
+}
+
+__device__ __forceinline__ DnTask dn_task(const MoeGemmArgs &a, const MoeTask &mt,
+                                          int32_t (&ent)[2], int spt)
+{
+    DnTask t;
+    const int rem = static_cast<int>((a.N - mt.n0 + 127) / 128);
+    t.nct = rem < kDnCT ? rem : kDnCT;
+    t.total = t.nct * spt;
+    t.n0 = mt.n0;
+    const int64_t boff = static_cast<int64_t>(mt.e) * a.N * a.K + mt.n0 * a.K;
+    t.rb = tile_rsrc(a.B0 + boff, (int64_t)t.nct * 128, a.K);
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t ebytes = a.a_rows_total * a.N * 4;
+    if (ebytes > 0xffffffffLL)
+        ebytes = 0xffffffffLL;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = wave * 32 + i * 16 + (lane & 15);
+        ent[i] = r < mt.nvalid ? a.rows[static_cast<int64_t>(mt.e) * a.T + mt.m0 + r] : -1;
+        t.eoff[i] = ent[i] >= 0
+                        ? (uint32_t)((int64_t)ent[i] * a.N * 4) + (uint32_t)(16 * (lane >> 4))
+                        : (uint32_t)ebytes;
+    }
+    return t;
+}
+
+__device__ __forceinline__ void dn_row_bases(const MoeGemmArgs &a, const int32_t (&ent)[2],
+                                             uint32_t (&base)[2])
+{
+    int64_t abytes = a.a_rows_total * a.K * 2;
+    if (abytes > 0xffffffffLL)
+        abytes = 0xffffffffLL;
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        base[i] = ent[i] >= 0 ? (uint32_t)((int64_t)ent[i] * a.K * 2) + (uint32_t)((lane >> 4) * 16)
+                              : (uint32_t)abytes;
+}
+
+// One task on the rows in `rows` (loads in flight; their first use waits).
+template <int KS, int LOG>
+__device__ __forceinline__ void dn_run(const DnTask &t, const DnCtx &x, const DnRows<KS> &rows)
+{
+    constexpr int SPT = KS / 2;
+    for (int g = 0; g < 4; ++g)
+        if (g < t.total)
+            for (int q = 0; q < 4; ++q)
+                dn_dma(t.rb, x.voff, x.lds, g, SPT, x.K, q);
+    // stage 0 landed (the task's rows too: a use of them waits by itself)
+    dn_vm_barrier((t.total > 1 ? 4 : 0) + (t.total > 2 ? 4 : 0) + (t.total > 3 ? 4 : 0));
+    DnFrags f0, f1;
+    dn_frag<0>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frag<1>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frag<2>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frag<3>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frag<4>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frag<5>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frag<6>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frag<7>(f0, x.lds_base + x.rowb + x.ch0);
+    dn_frags_wait(f0);
+    for (int c = 0; c < t.nct; ++c) {
+        DnAcc stk[LOG > 0 ? LOG : 1];
+        DnAcc acc;
+        dn_stages<KS, LOG, 0>(acc, stk, rows, f0, f1, c * SPT, t, x);
+        const uint32_t soff = (uint32_t)((t.n0 + 128 * c) * 4);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                __builtin_amdgcn_raw_buffer_store_b128(reinterpret_cast<const u32x4 &>(acc.v[i][j]),
+                                                       x.re, t.eoff[i] + j * 64, soff, 0);
+    }
+    // every ring load has landed and every wave is done with the ring
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Persistent over the down tasks (the XCD-aware split of moe_expert_kernel),
@@ -1037,100 +1130,48 @@ __global__ __launch_bounds__(256, 1) void moe_down_reg_kernel(MoeGemmArgs a,
     const int slots = gridDim.x / kXcds;
     const int per = (total_tasks + kXcds - 1) / kXcds;
     const int end = (xcd + 1) * per < total_tasks ? (xcd + 1) * per : total_tasks;
-    const int64_t K = a.K;
-    const uint32_t lds_base = lds_addr(lds);
-    int64_t abytes = a.a_rows_total * K * 2;
-    if (abytes > 0xffffffffLL)
-        abytes = 0xffffffffLL;
-    int64_t ebytes = a.a_rows_total * a.N * 4;
-    if (ebytes > 0xffffffffLL)
-        ebytes = 0xffffffffLL;
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.A), (short)0, (int)(uint32_t)abytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t re =
-        __builtin_amdgcn_make_buffer_rsrc(a.out, (short)0, (int)(uint32_t)ebytes, 0x00020000);
-    for (int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds; w < end; w += slots) {
-        const MoeTask t = moe_task(tiles, counts, w, ntn, TN);
-        const int nct = static_cast<int>((a.N - t.n0 + 127) / 128) < kDnCT
-                            ? static_cast<int>((a.N - t.n0 + 127) / 128)
-                            : kDnCT;
-        const int total = nct * SPT;
+    int w = xcd * per + static_cast<int>(blockIdx.x) / kXcds;
+    if (w >= end)
+        return;
+
+    DnCtx x;
+    x.K = a.K;
+    x.lds = lds;
+    x.lds_base = lds_addr(lds);
+    {
+        int64_t abytes = a.a_rows_total * a.K * 2;
+        if (abytes > 0xffffffffLL)
+            abytes = 0xffffffffLL;
+        int64_t ebytes = a.a_rows_total * a.N * 4;
+        if (ebytes > 0xffffffffLL)
+            ebytes = 0xffffffffLL;
+        x.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.A), (short)0,
+                                                 (int)(uint32_t)abytes, 0x00020000);
+        x.re = __builtin_amdgcn_make_buffer_rsrc(a.out, (short)0, (int)(uint32_t)ebytes, 0x00020000);
         const int lane = lane_id();
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-        const int wr = wave >> 1, wc = wave & 1;
-        // this lane's four rows (one per row block) and their entries
-        int32_t ent[4];
+        const uint32_t c = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wr * 64 + i * 16 + (lane & 15);
-            ent[i] = r < t.nvalid ? a.rows[static_cast<int64_t>(t.e) * a.T + t.m0 + r] : -1;
-        }
-        // the Wd rows of the task's column tiles
-        const int64_t boff = static_cast<int64_t>(t.e) * a.N * K + t.n0 * K;
-        const __amdgpu_buffer_rsrc_t rb = tile_rsrc(a.B0 + boff, (int64_t)nct * 128, K);
-        uint32_t voff[4];
-        {
-            const uint32_t c = (lane & 7) ^ (lane >> 3);
+        for (int q = 0; q < 4; ++q)
+            x.voff[q] = (uint32_t)((int64_t)(32 * wave + 8 * q + (lane >> 3)) * a.K * 2) + c * 16;
+        x.ch0 = (uint32_t)(((lane >> 4) ^ (lane & 7)) << 4);
+        x.ch1 = x.ch0 ^ 64u;
+        x.rowb = (uint32_t)(lane & 15) * kRowBytes;
+        x.l1 = x.lds_base + kDnBuf * kDnStage + wave * 16384 + lane * 16;
+    }
+
+    DnRows<KS> rows;
+    int32_t ent[2];
+    uint32_t base[2];
+    for (; w < end; w += slots) {
+        const DnTask t = dn_task(a, moe_task(tiles, counts, w, ntn, TN), ent, SPT);
+        dn_row_bases(a, ent, base);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                voff[q] = (uint32_t)((int64_t)(32 * wave + 8 * q + (lane >> 3)) * K * 2) + c * 16;
-        }
-        for (int g = 0; g < 4; ++g)
-            if (g < total)
-                dn_dma(rb, voff, lds, g, SPT, K);
-        // the rows, once (past the bucket: an offset past the range reads zero)
-        DnRows<KS> rows;
-        {
-            const uint32_t oob = (uint32_t)abytes;
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t base =
-                    ent[i] >= 0 ? (uint32_t)((int64_t)ent[i] * K * 2) + (uint32_t)((lane >> 4) * 16)
-                                : oob;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, base + ks * 64, 0, 0);
-                    rows.v[i][ks] = reinterpret_cast<const bf16x8 &>(v);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    asm volatile("" : "+a"(rows.v[i][ks]));
-        }
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        const uint32_t ch0 = (uint32_t)(((lane >> 4) ^ (lane & 7)) << 4);
-        const uint32_t ch1 = ch0 ^ 64u;
-        const uint32_t rowb = (uint32_t)(wc * 64 + (lane & 15)) * kRowBytes;
-        const uint32_t l1 = lds_base + kDnBuf * kDnStage + wave * 16384 + lane * 16;
-        DnFrags f0, f1;
-        dn_frag<0>(f0, lds_base + rowb + ch0);
-        dn_frag<1>(f0, lds_base + rowb + ch0);
-        dn_frag<2>(f0, lds_base + rowb + ch0);
-        dn_frag<3>(f0, lds_base + rowb + ch0);
-        dn_frags_wait(f0);
-        // output offsets: row ent[i], columns n0 + 128 c + 64 wc + 4 (lane >> 4) + 16 j
-        uint32_t eoff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            eoff[i] = ent[i] >= 0 ? (uint32_t)((int64_t)ent[i] * a.N * 4) +
-                                        (uint32_t)((wc * 64 + 4 * (lane >> 4)) * 4)
-                                  : (uint32_t)ebytes;
-        for (int c = 0; c < nct; ++c) {
-            DnAcc stk[LOG > 0 ? LOG : 1];
-            DnAcc acc;
-            dn_stages<KS, LOG, 0>(acc, stk, rows, f0, f1, c * SPT, total, lds_base, rowb, ch0,
-                                  ch1, rb, voff, lds, K, l1);
-            const uint32_t soff = (uint32_t)((t.n0 + 128 * c) * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        reinterpret_cast<const u32x4 &>(acc.v[i][j]), re, eoff[i] + j * 64, soff, 0);
-        }
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+            for (int ks = 0; ks < KS; ++ks)
+                dn_row_load<KS>(rows, x.ra, base, i, ks);
+        dn_run<KS, LOG>(t, x, rows);
     }
 }
 
