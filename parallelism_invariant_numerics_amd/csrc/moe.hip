@@ -822,8 +822,9 @@ __global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
 // task's rows of h (K = I = 32 KS) in AGPRs, for all the task's column
 // tiles (each wave loads only its own rows); the Wd rows stream through a
 // ring of four 16 KiB LDS stages (128 rows x 64 k, chunk-swizzled as in
-// gemm_core.hpp), one column tile after another without draining.  The MFMA
-// takes the weights as its first operand and the rows as its second: every output element is
+// gemm_core.hpp), one column tile after another without draining; every
+// wave reads all 128 columns of each stage.  The MFMA takes the weights as
+// its first operand and the rows as its second: every output element is
 // still the same products summed in the same k order from +0.0 (the same
 // leaves and tree as every other kernel), and a lane's four accumulator
 // values are four consecutive output columns of one row, which leave as one
