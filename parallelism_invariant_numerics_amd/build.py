@@ -63,6 +63,13 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def device_asm(source: str, out_path: str) -> str:
+    """The gfx950 assembly of one device source, with the library's flags."""
+    _run([HIPCC, *COMMON, *DEVICE_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, source),
+          "-o", out_path])
+    return out_path
+
+
 # CPU build of the host code under AddressSanitizer and UndefinedBehavior-
 # Sanitizer: the C ABI's checks, the identities and SHA-256, with the kernel
 # launchers replaced by stubs that launch nothing (host_stubs.cpp).  g++ on

@@ -530,7 +530,11 @@ __device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tm, int tn, i
 // global-to-LDS loads are in flight: the compiler would otherwise make every
 // LDS access there wait for them (it cannot tell the buffers apart).  Reads
 // are issued, then lds_wait() completes them and pins the results, so that
-// no use is scheduled before the wait.
+// no use is scheduled before the wait.  The compiler still takes a read's
+// output as written when the asm statement ends, so under register pressure
+// it may copy or spill it before the wait; the CPU test suite scans the
+// assembly of every kernel for that, and where it happens the reads and their
+// wait go into one asm statement instead.
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(ISO_LDS const char *)p;

@@ -103,13 +103,23 @@ __device__ __forceinline__ void dma_w(const PipeW &p, __amdgpu_buffer_rsrc_t rz,
 }
 
 // acc (AGPRs) += a b, or acc = a b from +0.0 for a leaf's first k-step.
-template <bool FRESH>
+// With TR the B block is the MFMA's first operand: the same products summed
+// in the same order into the same element, held transposed (a lane's four
+// values are four consecutive columns of one row).
+template <bool FRESH, bool TR = false>
 __device__ __forceinline__ void mfma_w(f32x4 &acc, const bf16x8 &a, const bf16x8 &b)
 {
-    if constexpr (FRESH)
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "v"(b));
-    else
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    if constexpr (TR) {
+        if constexpr (FRESH)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(b), "v"(a));
+        else
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+    } else {
+        if constexpr (FRESH)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&a"(acc) : "v"(a), "v"(b));
+        else
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    }
 }
 
 // Fragment read R of a k-step: R < 4 is A block R, else B block R - 4.
@@ -127,14 +137,14 @@ __device__ __forceinline__ void frag_w(FragsW &f, uint32_t aa, uint32_t ab)
 // One k-step: 32 MFMAs on f; after MFMA m < 18 one memory instruction, in
 // the order read, read, load: the 12 fragment reads into fn (addresses aa,
 // ab) and ring loads q0 .. q0+5 of stage dst.
-template <bool FRESH>
+template <bool FRESH, bool TR = false>
 __device__ __forceinline__ void kstep_w(AccW &acc, const FragsW &f, FragsW &fn, uint32_t aa,
                                         uint32_t ab, const PipeW &p, __amdgpu_buffer_rsrc_t rz,
                                         char *lds, int dst, int nst, int q0)
 {
     static_for<32>([&](auto Mc) {
         constexpr int m = decltype(Mc)::value;
-        mfma_w<FRESH>(acc.v[m / 8][m % 8], f.a[m / 8], f.b[m % 8]);
+        mfma_w<FRESH, TR>(acc.v[m / 8][m % 8], f.a[m / 8], f.b[m % 8]);
         if constexpr (m < 18) {
             if constexpr (m % 3 == 2)
                 dma_w(p, rz, lds, dst, nst, q0 + m / 3);
@@ -229,18 +239,18 @@ __device__ __forceinline__ void tree_push_w(AccW (&stk)[LOG > 0 ? LOG : 1], AccW
 // second k-step of stage t-3 and the first of stage t-2, and at the barrier
 // of stage st the 12 loads of stage st+2 are the only ones issued after
 // stage st+1's.
-template <bool FRESH>
+template <bool FRESH, bool TR = false>
 __device__ __forceinline__ void stage_w(AccW &acc, FragsW &f0, FragsW &f1, int st, int nst,
                                         uint32_t lds_base, uint32_t rowa, uint32_t rowb,
                                         uint32_t ch0, uint32_t ch1, const PipeW &p,
                                         __amdgpu_buffer_rsrc_t rz, char *lds)
 {
     const uint32_t bs = lds_base + (uint32_t)(st % kWBuf) * kWStageBytes;
-    kstep_w<FRESH>(acc, f0, f1, bs + rowa + ch1, bs + rowb + ch1, p, rz, lds, st + 2, nst, 6);
+    kstep_w<FRESH, TR>(acc, f0, f1, bs + rowa + ch1, bs + rowb + ch1, p, rz, lds, st + 2, nst, 6);
     frags_wait_w(f1);
     vm_barrier_w<12>();
     const uint32_t bn = lds_base + (uint32_t)((st + 1) % kWBuf) * kWStageBytes;
-    kstep_w<false>(acc, f1, f0, bn + rowa + ch0, bn + rowb + ch0, p, rz, lds, st + 3, nst, 0);
+    kstep_w<false, TR>(acc, f1, f0, bn + rowa + ch0, bn + rowb + ch0, p, rz, lds, st + 3, nst, 0);
     frags_wait_w(f0);
 }
 
@@ -253,9 +263,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t empty_rsrc()
 // The contraction of one 128 x 256 tile over 2^LOG leaves of `spl` stages
 // each.  On return `root` holds the subtree root (wave (wr, wc) holds rows
 // 64 wr + 16 i + 4 (lane >> 4) + r, columns 128 wc + 16 j + (lane & 15) in
-// v[i][j][r]), every load of this wave has landed and all waves have passed
-// a final barrier, so `lds` may be reused.
-template <int LOG>
+// v[i][j][r]; with TR row 64 wr + 16 i + (lane & 15), columns 128 wc + 16 j
+// + 4 (lane >> 4) + r), every load of this wave has landed and all waves
+// have passed a final barrier, so `lds` may be reused.
+template <int LOG, bool TR = false>
 __device__ __forceinline__ void leaf_tree_mainloop_w(const PipeW &p, int spl, char *lds,
                                                      AccW &root)
 {
@@ -287,10 +298,10 @@ __device__ __forceinline__ void leaf_tree_mainloop_w(const PipeW &p, int spl, ch
     AccW acc;
     static_for<LP>([&](auto Jc) {
         constexpr int J = decltype(Jc)::value;
-        stage_w<true>(acc, f0, f1, J * spl, nst, lds_base, rowa, rowb, ch0, ch1, p, rz, lds);
+        stage_w<true, TR>(acc, f0, f1, J * spl, nst, lds_base, rowa, rowb, ch0, ch1, p, rz, lds);
         for (int s = 1; s < spl; ++s)
-            stage_w<false>(acc, f0, f1, J * spl + s, nst, lds_base, rowa, rowb, ch0, ch1, p, rz,
-                           lds);
+            stage_w<false, TR>(acc, f0, f1, J * spl + s, nst, lds_base, rowa, rowb, ch0, ch1, p, rz,
+                               lds);
         mfma_drain_w(acc);
         if constexpr (J < LP - 1)
             tree_push_w<LOG, J, 0>(stk, acc);

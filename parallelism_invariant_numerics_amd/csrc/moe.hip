@@ -700,85 +700,77 @@ __device__ __forceinline__ PipeW moe_gu_pipe_w(const MoeGemmArgs &a, const MoeTa
     return p;
 }
 
-// h for the task's rows into `stg` (32 KiB of LDS: 128 rows of 128 bf16;
-// 16-byte chunk q of row r at q ^ (2 ((r >> 2) & 3))), then 16-byte stores of
-// the valid rows to h[rows_s[r]][n0 ..].  LDS accesses are inline assembly
-// (the next task's ring loads are in flight); ends with a barrier.
-__device__ __forceinline__ void moe_gu_epilogue_w(const MoeGemmArgs &a, const MoeTask &t,
-                                                  const AccW &r, const int32_t *rows_s, char *stg)
+// h of a wide task straight from the transposed accumulators (no staging):
+// lane l of wave (wr, wc) holds, for row block i, G (block 2k) and U (block
+// 2k + 1) of the four h columns 16 (4 wc + k) + 4 (l >> 4) + q of row 64 wr
+// + 16 i + (l & 15), which leave as one 8-byte store.
+__device__ __forceinline__ void moe_gu_epilogue_t(const MoeGemmArgs &a, const MoeTask &t,
+                                                  const AccW &r, const int32_t *rows_s)
 {
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = wave >> 1, wc = wave & 1;
-    const uint32_t sb = lds_addr(stg);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t hv = f32_to_bf16_rne(swiglu_act(r.v[i][2 * k][q], r.v[i][2 * k + 1][q]));
-                const int row = wr * 64 + i * 16 + (lane >> 4) * 4 + q;
-                const int col = (4 * wc + k) * 16 + (lane & 15);
-                const int chunk = (col >> 3) ^ (((row >> 2) & 3) << 1);
-                asm volatile("ds_write_b16 %0, %1" ::"v"(sb + row * 256 + chunk * 16 + (col & 7) * 2),
-                             "v"(hv)
-                             : "memory");
-            }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // h through a buffer resource: 32-bit offsets, no 64-bit address registers
+    // the four bucket entries of this lane's rows, read and waited for in
+    // one asm statement (an output of an LDS read left in flight across
+    // statements may be copied before it has arrived)
+    int32_t dst[4];
+    {
+        const uint32_t e0 = lds_addr(rows_s + wr * 64 + (lane & 15));
+        asm volatile("ds_read_b32 %0, %4\n\t"
+                     "ds_read_b32 %1, %4 offset:64\n\t"
+                     "ds_read_b32 %2, %4 offset:128\n\t"
+                     "ds_read_b32 %3, %4 offset:192\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(dst[0]), "=&v"(dst[1]), "=&v"(dst[2]), "=&v"(dst[3])
+                     : "v"(e0)
+                     : "memory");
+    }
     int64_t hbytes = a.a_rows_total * a.row_div * a.N * 2;
     if (hbytes > 0xffffffffLL)
         hbytes = 0xffffffffLL;
     const __amdgpu_buffer_rsrc_t hr =
         __builtin_amdgcn_make_buffer_rsrc(a.out, (short)0, (int)(uint32_t)hbytes, 0x00020000);
-    const bool al = (reinterpret_cast<uintptr_t>(a.out) % 16 == 0) && (a.N % 8 == 0) &&
-                    (t.n0 % 8 == 0);
+    const bool al = (reinterpret_cast<uintptr_t>(a.out) % 8 == 0) && (a.N % 4 == 0) &&
+                    (t.n0 % 4 == 0);
     const int cmax = a.N - t.n0 < kGuColsW ? static_cast<int>(a.N - t.n0) : kGuColsW;
-    constexpr int UPT = BM * (kGuColsW / 8) / 256;  // 16-byte units per thread
-    // the thread index through lane_id(): addresses derived from it are not
-    // hoisted out of the task loop (where they would only be spilled)
-    const int tid = wave * 64 + lane;
-    u32x4 v[UPT];
-    int32_t dst[UPT];
 #pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-        const int u = tid + k * 256;
-        const int row = u >> 4, q = u & 15;
-        asm volatile("ds_read_b128 %0, %1"
-                     : "=v"(v[k])
-                     : "v"(sb + row * 256 + ((q ^ (((row >> 2) & 3) << 1)) << 4)));
-        lds_issue_b32(dst[k], lds_addr(rows_s + row));
-    }
-    lds_wait();
-#pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-        lds_pin(v[k]);
-        lds_pin(dst[k]);
-        const int u = tid + k * 256;
-        const int row = u >> 4, q = u & 15;
-        if (row >= t.nvalid)
+    for (int i = 0; i < 4; ++i) {
+        if (wr * 64 + i * 16 + (lane & 15) >= t.nvalid)
             continue;
-        const uint32_t off = (uint32_t)((dst[k] * a.N + t.n0 + 8 * q) * 2);
-        if (al && 8 * q + 8 <= cmax) {
-            __builtin_amdgcn_raw_buffer_store_b128(v[k], hr, off, 0, 0);
-        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (e < cmax - 8 * q)
-                    __builtin_amdgcn_raw_buffer_store_b16(
-                        static_cast<uint16_t>(v[k][e >> 1] >> (16 * (e & 1))), hr, off + 2 * e, 0, 0);
+        for (int k = 0; k < 4; ++k) {
+            uint32_t hv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                hv[q] = f32_to_bf16_rne(swiglu_act(r.v[i][2 * k][q], r.v[i][2 * k + 1][q]));
+            const int col = (4 * wc + k) * 16 + 4 * (lane >> 4);
+            const uint32_t off = (uint32_t)((dst[i] * a.N + t.n0 + col) * 2);
+            if (al && col + 4 <= cmax) {
+                u32x2 v;
+                v[0] = hv[0] | (hv[1] << 16);
+                v[1] = hv[2] | (hv[3] << 16);
+                __builtin_amdgcn_raw_buffer_store_b64(v, hr, off, 0, 0);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (col + q < cmax)
+                        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hv[q]), hr,
+                                                              off + 2 * q, 0, 0);
+            }
         }
     }
+    // the next task's bucket entries go into the other half of rows_s only
+    // after every wave has read this half
     __builtin_amdgcn_s_barrier();
 }
 
 // Persistent over the wide gate/up tasks, one workgroup per CU, with the
 // XCD-aware task split of moe_expert_kernel.  The next task's bucket entries
-// are fetched during the main loop; the epilogue stages h through the third
-// ring slot.  (Requesting the next task's first ring stages before the
-// epilogue measured no faster, and a register reload in the epilogue would
-// then wait for those loads.)
+// are fetched during the main loop; the MFMAs take the weights as their
+// first operand, so the epilogue stores h straight from registers.
+// (Requesting the next task's first ring stages before the epilogue measured
+// no faster, and a register reload in the epilogue would then wait for those
+// loads.)
 template <int LOG>
 __global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
                                                              const int32_t *__restrict__ tiles,
@@ -787,7 +779,6 @@ __global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
 {
     __shared__ __attribute__((aligned(16))) char lds[kWLdsBytes];
     __shared__ int32_t rows_s[2][BM];
-    char *stg = lds + 2 * kWStageBytes;
     const int ntn = static_cast<int>((a.N + kGuColsW - 1) / kGuColsW);
     const int total = __builtin_amdgcn_readfirstlane(*ntiles) * ntn;
     const int xcd = blockIdx.x % kXcds;
@@ -807,8 +798,8 @@ __global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
         if (wn < end)
             rows_dma(a, moe_task(tiles, counts, wn, ntn, kGuColsW), rows_s[b ^ 1]);
         AccW r0;
-        leaf_tree_mainloop_w<LOG>(p, a.stages_per_leaf, lds, r0);
-        moe_gu_epilogue_w(a, t, r0, rows_s[b], stg);
+        leaf_tree_mainloop_w<LOG, true>(p, a.stages_per_leaf, lds, r0);
+        moe_gu_epilogue_t(a, t, r0, rows_s[b]);
         if (wn >= end)
             break;
         w = wn;
