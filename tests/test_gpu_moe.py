@@ -59,7 +59,9 @@ def _check_stages(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, y, st, what):
     E, I, _ = Wg.shape
     idx, gate = oracle.moe_route(lg, k)
     assert np.array_equal(st["idx"], idx), what
-    assert np.allclose(st["gate"], gate, rtol=4e-7, atol=0), what
+    # FP32 gates: 4e-7 relative, and nothing below FP32's smallest normal number
+    # (an FP32 softmax of very spread logits gives 0 where float64 keeps ~1e-45)
+    assert np.allclose(st["gate"], gate, rtol=4e-7, atol=2.0 ** -126), what
     cg = iso.contract(Lgu, H // Lgu, 0)
     cd = iso.contract(Ldn, I // Ldn, 0)
     act_or, _ = oracle.moe_gate_up(X, Wg, Wu, idx, Lgu)
@@ -140,6 +142,42 @@ def test_top1_and_identical_experts():
     for s in range(1, 4):  # every expert computes the same bits for a token
         assert np.array_equal(st4["e"][:, s].view(np.uint32), st4["e"][:, 0].view(np.uint32))
     assert np.allclose(y4, st4["e"][:, 0], rtol=4 * 2.0 ** -23, atol=1e-30)
+
+
+def test_degenerate_routing():
+    """Routing extremes through the wide gate/up and register down kernels (H = 1024,
+    I = 512, 4 leaves each): every token on the same k experts (three row tiles each,
+    the other experts empty), a single token, top-k equal to the expert count, and an
+    empty batch; every stage against the oracle."""
+    H, I = 1024, 512
+    T, E, k = 300, 16, 4
+    X = normal_bf16(41, (T, H), 1.0)
+    lg = normal_f32(42, (T, E)) * np.float32(0.01)
+    lg[:, :k] += np.float32(10.0) - np.arange(k, dtype=np.float32)
+    Wg = normal_bf16(43, (E, I, H), 0.05)
+    Wu = normal_bf16(44, (E, I, H), 0.05)
+    Wd = normal_bf16(45, (E, H, I), 0.05)
+    note("moe skewed routing: every token on experts 0..3")
+    y, st = _run(X, lg, Wg, Wu, Wd, k, 4, 4)
+    assert np.array_equal(np.sort(st["idx"], axis=1), np.tile(np.arange(k), (T, 1)))
+    _check_stages(X, lg, Wg, Wu, Wd, k, 4, 4, y, st, "skewed")
+    note("moe one token")
+    y1, st1 = _run(X[:1], lg[:1] * np.float32(100.0), Wg, Wu, Wd, k, 4, 4)
+    _check_stages(X[:1], lg[:1] * np.float32(100.0), Wg, Wu, Wd, k, 4, 4, y1, st1, "one token")
+    note("moe top-k equal to the expert count")
+    E4 = 4
+    lg4 = normal_f32(46, (37, E4))
+    y4, st4 = _run(X[:37], lg4, Wg[:E4], Wu[:E4], Wd[:E4], E4, 4, 4)
+    _check_stages(X[:37], lg4, Wg[:E4], Wu[:E4], Wd[:E4], E4, 4, 4, y4, st4, "k = E")
+    note("moe empty batch")
+    t = torch()
+    cg = iso.contract(4, H // 4, 0)
+    cd = iso.contract(4, I // 4, 0)
+    ws = t.empty(max(iso.moe_workspace(0, H, E, I, k), 1), dtype=t.uint8, device="cuda")
+    y0 = iso.moe_combine(dev(X[:0]), t.from_numpy(lg[:0]).to("cuda"), dev(Wg), dev(Wu), dev(Wd), k,
+                         cg, cd, workspace=ws)
+    t.cuda.synchronize()
+    assert tuple(y0.shape) == (0, H)
 
 
 def test_token_orderings_bitwise():
