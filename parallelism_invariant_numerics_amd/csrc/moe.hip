@@ -798,7 +798,12 @@ __global__ __launch_bounds__(256, 1) void moe_gu_wide_kernel(MoeGemmArgs a,
         if (wn < end)
             rows_dma(a, moe_task(tiles, counts, wn, ntn, kGuColsW), rows_s[b ^ 1]);
         AccW r0;
-        leaf_tree_mainloop_w<LOG, true>(p, a.stages_per_leaf, lds, r0);
+        // stages per leaf as a value the compiler re-reads for every task:
+        // conditions derived from it would otherwise be hoisted out of the
+        // task loop and spilled, and their reload waits for every load
+        int spl = a.stages_per_leaf;
+        asm volatile("" : "+s"(spl));
+        leaf_tree_mainloop_w<LOG, true>(p, spl, lds, r0);
         moe_gu_epilogue_t(a, t, r0, rows_s[b]);
         if (wn >= end)
             break;
