@@ -630,17 +630,19 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(
         const MoeTask t = moe_task(tiles, counts, w, ntn, TN);
         const int wn = w + slots;
         Acc<C> r0;
+        // re-read per task (see moe_gu_wide_kernel)
+        int spl = a.stages_per_leaf;
+        asm volatile("" : "+s"(spl));
         if constexpr (OVERLAP) {
             const Pipe p = moe_pipe<C, GATE_UP>(a, t, rows_s[b]);
             if (wn < end)
                 rows_dma(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]);
-            leaf_tree_mainloop<C, LOG, false>(p, a.stages_per_leaf, lds, r0);
+            leaf_tree_mainloop<C, LOG, false>(p, spl, lds, r0);
             if (wn < end)
                 pipe_prologue<C>(moe_pipe<C, GATE_UP>(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]),
                                  lds, nst);
         } else {
-            leaf_tree_mainloop<C, LOG>(moe_pipe<C, GATE_UP>(a, t, rows_s[b]), a.stages_per_leaf,
-                                       lds, r0);
+            leaf_tree_mainloop<C, LOG>(moe_pipe<C, GATE_UP>(a, t, rows_s[b]), spl, lds, r0);
             if (wn < end)
                 rows_dma(a, moe_task(tiles, counts, wn, ntn, TN), rows_s[b ^ 1]);
         }
