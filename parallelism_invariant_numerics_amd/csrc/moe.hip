@@ -661,9 +661,9 @@ __global__ __launch_bounds__(C::kThreads, 2) void moe_expert_kernel(
 // rows are 16-row blocks that alternate between Wg and Wu: block 2k holds Wg
 // rows n0 + 16k .. n0 + 16k + 15 and block 2k+1 the same Wu rows.  Wave
 // column wc then holds G in its column blocks 2k and U in blocks 2k+1 for
-// the same intermediate columns n0 + 16 (4 wc + k) + (lane & 15), and
-// h = bf16(silu(G) U) is formed in registers (the same device function as
-// every other SwiGLU here).
+// the same intermediate columns n0 + 16 (4 wc + k) .. + 15, element for
+// element in matching registers, and h = bf16(silu(G) U) is formed in
+// registers (the same device function as every other SwiGLU here).
 constexpr int kGuColsW = 128;
 
 // Ring loads of a wide gate/up task: A rows gathered as in moe_pipe; B group
