@@ -70,7 +70,14 @@ __global__ __launch_bounds__(C::kThreads, 2) void gemm_leaf_kernel(GemmParams p)
     const Pipe pipe = make_pipe<C>(p.A + m0 * p.K, p.M - m0, p.Wt + n0 * p.K, p.N - n0, p.K,
                                       part * p.k_per_part);
     Acc<C> root;
-    leaf_tree_mainloop<C, LOG>(pipe, p.stages_per_leaf, lds, root);
+    // a wave whose rows all lie past the matrix edge (a tile of at most 64
+    // rows) only keeps the ring going: its fragment reads would take LDS
+    // bandwidth from the waves that have rows
+    const int wr = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) / C::WC;
+    if (p.M - m0 <= static_cast<int64_t>(wr) * (BM / C::WR))
+        leaf_tree_mainloop<C, LOG, true, true>(pipe, p.stages_per_leaf, lds, root);
+    else
+        leaf_tree_mainloop<C, LOG>(pipe, p.stages_per_leaf, lds, root);
 
     if (p.mode == kOutWorkspace) {
         float *ws = static_cast<float *>(p.out) + (static_cast<int64_t>(part) * p.M + m0) * p.N + n0;

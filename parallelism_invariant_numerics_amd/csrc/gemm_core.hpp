@@ -306,7 +306,12 @@ __device__ __forceinline__ void pipe_prologue(const Pipe &p, char *lds, int nst)
 // the barrier: while one wave of a SIMD waits on the address unit, the other
 // one keeps the matrix core busy.  The loads still go out before the next
 // stage's wait, so the ring's counts are unchanged.
-template <class C, int LOG, bool PROLOGUE = true>
+// With IDLE the wave owns no row of the tile (all of its rows lie past the
+// matrix edge): it issues exactly the ring loads and barriers of the other
+// waves, in the same order, and no fragment read or MFMA, so the stage ring
+// keeps its counts while the LDS serves only the waves with rows; `root` is
+// zero and never stored.
+template <class C, int LOG, bool PROLOGUE = true, bool IDLE = false>
 __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char *lds,
                                                    Acc<C> &root)
 {
@@ -328,6 +333,18 @@ __device__ __forceinline__ void leaf_tree_mainloop(const Pipe &p, int spl, char 
 
     if constexpr (PROLOGUE)
         pipe_prologue<C>(p, lds, nst);
+
+    if constexpr (IDLE) {
+        for (int st = 0; st < nst; ++st) {
+            const int ahead = nst - 1 - st;
+            stage_barrier<C>(ahead < NB - 2 ? ahead : NB - 2);
+            if (st + NB - 1 < nst)
+                stage_dma<C>(p, lds, st + NB - 1, (st + NB - 1) % NB);
+        }
+        acc_zero(root);
+        __builtin_amdgcn_s_barrier();
+        return;
+    }
 
     Acc<C> stk[LOG > 0 ? LOG : 1];
     Acc<C> acc;
