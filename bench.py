@@ -97,7 +97,8 @@ def _settle(fn, seconds=None):
 def _time_events(fn, steps, stream):
     """Average duration (ms) of one fn() call: HIP events on `stream` around
     `steps` back-to-back calls (the launches queue up, so host-side call
-    overhead does not appear as idle GPU time between them)."""
+    overhead does not appear as idle GPU time between them as long as the
+    host issues calls faster than the GPU runs them)."""
     import torch
     _settle(fn, 0.66 * SETTLE_S)
     fn()
@@ -110,6 +111,25 @@ def _time_events(fn, steps, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def _abi_gemm(iso, c, A, W, out, ws, stream):
+    """A zero-argument call of iso_gemm through the C ABI with its arguments
+    marshalled once, as a C or C++ caller makes it: for calls of ~10 us the
+    Python binding's per-call work is about as long as the GPU's, so timing
+    through it measures the host."""
+    import ctypes
+    args = (ctypes.byref(c), A.data_ptr(), W.data_ptr(), out.data_ptr(),
+            iso.F32 if out.dtype == __import__("torch").float32 else iso.BF16,
+            A.shape[0], W.shape[0], A.shape[1], 1,
+            None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel(),
+            stream.cuda_stream)
+    f = iso.lib.iso_gemm
+
+    def call():
+        if f(*args) != 0:
+            raise RuntimeError("iso_gemm failed")
+    return call
 
 
 def _time_graph(fn, inner=20, replays=10, check=None, reset=None):
@@ -424,9 +444,15 @@ def main():
         o1 = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
         g_1 = lambda: iso.gemm(A1, Ws, cs, out=o1)
         g_1()
-        ms_1 = _time_events(g_1, max(10, args.steps), stream)
+        ms_1p = _time_events(g_1, max(10, args.steps), stream)
+        ok &= bool(torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
+        o1.zero_()
+        a_1 = _abi_gemm(iso, cs, A1, Ws, o1, None, stream)
+        a_1()
+        ms_1 = _time_events(a_1, max(10, args.steps), stream)
         ok &= bool(torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
         extra["sweep"]["row1_us"] = round(ms_1 * 1e3, 2)
+        extra["sweep"]["row1_binding_us"] = round(ms_1p * 1e3, 2)
         extra["sweep"]["row1_weight_gbs"] = round(4096 * Ks * 2 / (ms_1 * 1e-3) / 1e9, 1)
         gr = _time_graph(g_1, reset=o1.zero_,
                          check=lambda: torch.equal(o1.view(torch.int32), ref_s[:1].view(torch.int32)))
@@ -442,9 +468,15 @@ def main():
                               device="cuda")
             g_b = lambda: iso.gemm(Ab, Ws, cs, out=ob, workspace=wsb)
             g_b()
-            ms_b = _time_events(g_b, max(10, args.steps), stream)
+            ms_bp = _time_events(g_b, max(10, args.steps), stream)
+            ok &= bool(torch.equal(ob.view(torch.int32), ref_s[100:100 + mb].view(torch.int32)))
+            ob.zero_()
+            a_b = _abi_gemm(iso, cs, Ab, Ws, ob, wsb, stream)
+            a_b()
+            ms_b = _time_events(a_b, max(10, args.steps), stream)
             ok &= bool(torch.equal(ob.view(torch.int32), ref_s[100:100 + mb].view(torch.int32)))
             extra["sweep"][f"rows{mb}_us"] = round(ms_b * 1e3, 2)
+            extra["sweep"][f"rows{mb}_binding_us"] = round(ms_bp * 1e3, 2)
             extra["sweep"][f"rows{mb}_weight_gbs"] = round(4096 * Ks * 2 / (ms_b * 1e-3) / 1e9, 1)
             gr = _time_graph(g_b, reset=ob.zero_, check=lambda: torch.equal(ob.view(torch.int32),
                                                             ref_s[100:100 + mb].view(torch.int32)))
