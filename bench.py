@@ -695,7 +695,20 @@ def main():
             for p_ in range(T0, Tc):
                 iso.cpr_decode_step(qc, kc, vc, alc, bec, p_, sd, rd, cc, out=od[p_ - T0],
                                     workspace=wsd)
-        d_ms = _time_events(dec_chunk, 3, stream) / Cc
+        d_ms_p = _time_events(dec_chunk, 3, stream) / Cc
+        # the same steps through the C ABI with their arguments marshalled
+        # once (a step's kernel is shorter than the binding's per-call work)
+        import ctypes
+        dec_args = [(ctypes.byref(cc), qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), alc.data_ptr(),
+                     bec.data_ptr(), p_, sd.data_ptr(), rd.data_ptr(), od[p_ - T0].data_ptr(), Hc,
+                     wsd.data_ptr(), wsd.numel(), stream.cuda_stream) for p_ in range(T0, Tc)]
+        f_dec = iso.lib.iso_cpr_decode_step
+
+        def dec_chunk_abi():
+            for a_ in dec_args:
+                if f_dec(*a_) != 0:
+                    raise RuntimeError("iso_cpr_decode_step failed")
+        d_ms = _time_events(dec_chunk_abi, 3, stream) / Cc
         # FP32 operations per token and head: step ~7 d^2, chunk form ~7 d^2,
         # boundary pass 2 d^3 / C (d = 128, C = 64)
         c_ops = Tc * Hc * (14.0 * Dc * Dc + 2.0 * Dc ** 3 / Cc)
@@ -703,6 +716,7 @@ def main():
                         "prefill_ms": round(c_ms, 4),
                         "prefill_tokens_per_s": round(Tc / (c_ms * 1e-3), 1),
                         "decode_us_per_token": round(d_ms * 1e3, 2),
+                        "decode_binding_us_per_token": round(d_ms_p * 1e3, 2),
                         "alu_tops": round(c_ops / (c_ms * 1e-3) / 1e12, 2),
                         "alu_frac": round(c_ops / (c_ms * 1e-3) / 1e12 / PEAK_FP32_OPS_T, 4)}
         del qc, kc, vc, alc, bec, wsc, oc, snc, rnc, sd, rd, wsd, od
