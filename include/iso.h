@@ -215,9 +215,10 @@ iso_status iso_table_check(const iso_composition *table, size_t n, const char *r
  * for arguments iso_gemm would reject.  With P > 1 (or more than 16 leaves
  * per partition outside the few-rows kernel) the workspace is required.
  * With P = 1 on an output of fewer than 128 tiles of 128 x 128 and more
- * than 32 rows, the size returned lets the call split K into up to four
- * partitions of whole subtrees internally (same bits, more workgroups); a
- * call given less runs without that split. */
+ * than 16 rows (more than 32 on a layer of at most 8 MiB of weights), the
+ * size returned lets the call split K into up to eight (up to 64 rows) or
+ * four (more rows) partitions of whole subtrees internally (same bits, more
+ * workgroups); a call given less runs without that split. */
 size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int partitions);
 
 /*
@@ -228,12 +229,15 @@ size_t iso_gemm_workspace(const iso_contract *c, int64_t M, int64_t N, int parti
  * `partitions` P emulates P tensor-parallel ranks on this GPU: partition p
  * computes its subtree root into the workspace and a combine kernel applies
  * the top log2(P) levels.  Every P allowed by the claim gives the same bits.
- * The launch shape follows the problem (128 x 128 tiles; with P = 1 and up
- * to 32 rows -- or up to 96 rows without a workspace, 64 on a layer of at
- * most 8 MiB of weights -- one workgroup per 16 output columns streaming the
- * weights; with P = 1, a workspace and few output tiles, an internal split
- * of K), never the numbers: a row's bits do not depend on M, on its
- * position, or on which of these runs.
+ * The launch shape follows the problem, never the numbers: 128 x 128 or
+ * 128 x 256 tiles; with P = 1, for shapes the weight-streaming kernel takes
+ * (4 or 8-64 leaves of 64-512 columns, K <= 4096), one workgroup per 16
+ * output columns for up to 16 rows, up to 32 on a layer of at most 8 MiB of
+ * weights or without a workspace, and up to 96 without the split below on
+ * an output of fewer than 128 tiles with 8 or more leaves; with P = 1, a
+ * workspace and fewer than 128 output tiles, an internal split of K (see
+ * iso_gemm_workspace).  A row's bits do not depend on M, on its position,
+ * or on which of these runs.
  * Limits: M, N < 2^23 and (M/128)(N/128) < 2^28 tiles, K <= 2^22.
  */
 iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *C,
