@@ -84,6 +84,25 @@ def test_partitions_bitwise(L):
     assert np.array_equal(bf, f32_to_bf16_bits(base.view(np.float32)))
 
 
+def test_half_empty_tiles_bitwise():
+    """Row tiles with at most 64 rows (the lower waves of the tile then only keep the
+    stage ring going) under every partition count, FP32 and bf16: the same bits as the
+    same rows inside a batch of 600, and the oracle's values within tolerance."""
+    K, N, L = 2048, 384, 8
+    A = normal_bf16(31, (600, K), 1.0)
+    Wt = normal_bf16(32, (N, K), 0.02)
+    note("half-empty tiles")
+    big = u32(_run(A, Wt, L))
+    bigb = _run(A, Wt, L, 1, iso.BF16)
+    for m in (64, 129, 192):  # one 64-row tile; 128 + 1; 128 + 64
+        for P in (1, 2, 4, 8):
+            assert np.array_equal(u32(_run(A[:m], Wt, L, P)), big[:m]), (m, P)
+            assert np.array_equal(_run(A[:m], Wt, L, P, iso.BF16), bigb[:m]), (m, P, "bf16")
+    rows = np.array([0, 63, 128, 191])
+    check_gemm_tol(big[rows].view(np.float32), oracle.gemm(A[rows], Wt, L), absdot(A[rows], Wt),
+                   "half-empty tiles")
+
+
 def test_run_to_run_determinism():
     A = normal_bf16(7, (513, 2048), 1.0)
     Wt = normal_bf16(8, (257, 2048), 0.02)
