@@ -1262,8 +1262,11 @@ static void launch_down_reg(const MoeGemmArgs &a, hipStream_t stream)
 static hipError_t dispatch_down(const MoeGemmArgs &a, int leaves, hipStream_t stream)
 {
     const int KS = static_cast<int>(a.K / 32);
+    // the register kernel addresses e (rows x N FP32) with 32-bit offsets; past
+    // 4 GiB the expert kernel, which uses 64-bit pointers, takes the call
     const bool fits = (a.K == 128 || a.K == 256 || a.K == 512) && a.N % 128 == 0 &&
-                      (leaves == 1 || leaves == 2 || leaves == 4) && KS / leaves >= 2;
+                      (leaves == 1 || leaves == 2 || leaves == 4) && KS / leaves >= 2 &&
+                      a.a_rows_total * a.N * 4 <= 0xffffffffLL;
     if (!fits)
         return dispatch_expert<false>(a, leaves, stream);
     switch (KS * 8 + leaves) {

@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 iso = pytest.importorskip("parallelism_invariant_numerics_amd")
 
 
-def _run(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, dW=None):
+def _run(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, dW=None, stages=True):
     t = torch()
     T, H = X.shape
     E, I, _ = Wg.shape
@@ -39,6 +39,8 @@ def _run(X, lg, Wg, Wu, Wd, k, Lgu, Ldn, dW=None):
     ws = t.empty(iso.moe_workspace(T, H, E, I, k), dtype=t.uint8, device="cuda")
     y = iso.moe_combine(dev(X), t.from_numpy(lg).to("cuda"), *dW, k, cg, cd, workspace=ws)
     t.cuda.synchronize()
+    if not stages:
+        return host(y), None
     st = iso.moe_stages(ws, T, H, E, I, k)
     return host(y), {n: host(v) for n, v in st.items()}
 
@@ -178,6 +180,26 @@ def test_degenerate_routing():
                          cg, cd, workspace=ws)
     t.cuda.synchronize()
     assert tuple(y0.shape) == (0, H)
+
+
+def test_expert_outputs_past_4_gib():
+    """T * top_k * H FP32 expert outputs beyond 4 GiB (65600 tokens, top-8, H = 2048: e is
+    4.3 GB), which the down projection must address with 64-bit offsets: sampled tokens,
+    among them tokens whose outputs lie past 4 GiB, get the bits of a small batch of the
+    same tokens and the oracle's values within tolerance."""
+    T, H, E, I, k = 65600, 2048, 8, 128, 8
+    X = normal_bf16(51, (T, H), 1.0)
+    lg = normal_f32(52, (T, E))
+    Wg = normal_bf16(53, (E, I, H), 0.05)
+    Wu = normal_bf16(54, (E, I, H), 0.05)
+    Wd = normal_bf16(55, (E, H, I), 0.05)
+    dW = (dev(Wg), dev(Wu), dev(Wd))
+    note("moe with e past 4 GiB")
+    y, _ = _run(X, lg, Wg, Wu, Wd, k, 4, 2, dW, stages=False)
+    sel = np.array([0, 1, 32767, 40000, 65087, 65088, 65535, 65536, 65590, 65599])
+    ys, st = _run(X[sel], lg[sel], Wg, Wu, Wd, k, 4, 2, dW)
+    assert np.array_equal(y[sel].view(np.uint32), ys.view(np.uint32))
+    _check_stages(X[sel], lg[sel], Wg, Wu, Wd, k, 4, 2, ys, st, "past 4 GiB")
 
 
 def test_token_orderings_bitwise():
