@@ -267,16 +267,16 @@ __global__ __launch_bounds__(C::kThreads, 2) void lmhead_fused_kernel(LmArgs a)
 // same v_mfma_f32_16x16x32_bf16 chain per leaf in ascending k, the same
 // balanced tree over the leaves, the same chunk statistics), so the bits are
 // those of the fused kernel; only the data movement differs.  One workgroup
-// of 16 waves per CU walks the chunks (128 vocabulary ids each) in a
-// grid-stride loop.  Wave w takes the 16 ids n0 + 16 (w & 7) .. + 15 and the
-// leaves of half w >> 3 of the leaf block (a subtree of 2^(LOG-1) leaves);
-// the two half roots are added in the epilogue, the top tree level.  Weight
-// fragments go from HBM straight to registers, one leaf (KS k-steps) ahead,
-// so a CU keeps 16 x KS KiB of weights in flight; the rows (zero past M) sit
-// in LDS for the whole launch.  The chunk statistics use the balanced tree
-// over the eight 16-id blocks in id order, which is the fused kernel's tree.
+// of 8 waves per CU walks the chunks (128 vocabulary ids each) in a
+// grid-stride loop.  Wave w takes the 16 ids n0 + 16 w .. + 15 and all the
+// leaves, folded by the register tree.  Weight fragments go from HBM straight
+// to registers, one leaf (KS k-steps) ahead, so a CU keeps 8 x KS KiB of
+// weights in flight (16 waves, each on half of the leaves, kept twice as
+// much in flight and took 2-4 % longer); the rows (zero past M) sit in LDS
+// for the whole launch.  The chunk statistics use the balanced tree over the
+// eight 16-id blocks in id order, which is the fused kernel's tree.
 constexpr int kDecRows = 16;
-constexpr int kDecWaves = 16;
+constexpr int kDecWaves = 8;
 constexpr int64_t kDecMaxK = 4096;
 constexpr int kDecPitchMax = static_cast<int>(kDecMaxK) * 2 + 16;  // LDS bytes per row
 
@@ -288,15 +288,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v)
 template <int LOG, int KS>
 __global__ __launch_bounds__(kDecWaves * 64) void lmhead_decode_kernel(LmArgs a)
 {
-    static_assert(LOG >= 2, "two halves of at least two leaves");
-    constexpr int LH = 1 << (LOG - 1);  // leaves per half (even)
+    static_assert(LOG >= 1, "an even number of leaves");
+    constexpr int LH = 1 << LOG;  // leaves (even: leaf 0 of the next chunk lands in buffer 0)
     __shared__ __attribute__((aligned(16))) char arow[kDecRows * kDecPitchMax];
-    __shared__ __attribute__((aligned(16))) f32x4 xroot[8][64];
     __shared__ float red_m[8][kDecRows], red_s[8][kDecRows];
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int blk = wave & 7, half = wave >> 3;
+    const int blk = wave;
     const int64_t K = a.K;
     const int pitch = static_cast<int>(K) * 2 + 16;  // 16 bytes of padding: rows shift banks
 
@@ -320,7 +319,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void lmhead_decode_kernel(LmArgs a)
     // row (lane & 15) of the wave's 16 ids and the same k-group
     const uint32_t a_lds = lds_addr(arow) + static_cast<uint32_t>((lane & 15) * pitch + (lane >> 4) * 16);
     const uint32_t voff = static_cast<uint32_t>((lane & 15) * K * 2 + (lane >> 4) * 16);
-    const int kstep0 = half * LH * KS;  // this half's first k-step
 
     auto brsrc = [&](int64_t ch) {
         const int64_t col0 = ch * kChunk + 16 * blk;
@@ -332,7 +330,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void lmhead_decode_kernel(LmArgs a)
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
             dst[kk] = __builtin_amdgcn_raw_buffer_load_b128(
-                r, voff, static_cast<int>((kstep0 + leaf * KS + kk) * 64), 0);
+                r, voff, static_cast<int>((leaf * KS + kk) * 64), 0);
     };
 
     u32x4 bb[2][KS];
@@ -341,7 +339,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void lmhead_decode_kernel(LmArgs a)
     for (;;) {
         const int64_t cn = c + gridDim.x;
         const __amdgpu_buffer_rsrc_t rbn = brsrc(cn < a.nchunk ? cn : c);
-        f32x4 stk[LOG - 1];
+        f32x4 stk[LOG];
         f32x4 acc;
         static_for<LH>([&](auto Jc) {
             constexpr int J = decltype(Jc)::value;
@@ -356,16 +354,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void lmhead_decode_kernel(LmArgs a)
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 f32x4 av;
-                lds_issue_b128(av, a_lds + static_cast<uint32_t>((kstep0 + J * KS + kk) * 64));
+                lds_issue_b128(av, a_lds + static_cast<uint32_t>((J * KS + kk) * 64));
                 lds_wait();
                 lds_pin(av);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                               as_bf16x8(bb[cur][kk]), acc, 0, 0, 0);
             }
-            // binary-counter tree over the half's leaves (lower leaves left)
+            // binary-counter tree over the leaves (lower leaves left)
             bool done = false;
 #pragma unroll
-            for (int b = 0; b < LOG - 1; ++b) {
+            for (int b = 0; b < LOG; ++b) {
                 if (!done) {
                     if ((J >> b) & 1) {
                         acc = stk[b] + acc;
@@ -377,26 +375,22 @@ __global__ __launch_bounds__(kDecWaves * 64) void lmhead_decode_kernel(LmArgs a)
             }
         });
 
-        // epilogue: z = (first half) + (second half), then the chunk statistics
-        if (half == 1)
-            xroot[blk][lane] = acc;
+        // epilogue: the chunk statistics (the barrier first: wave 0 has read
+        // the previous chunk's block maxima and sums)
         lds_barrier();
         const int64_t n0 = c * kChunk;
         const int64_t col = n0 + 16 * blk + (lane & 15);
         const bool colv = col < a.V;
-        f32x4 z = acc;
-        if (half == 0) {
-            z = acc + xroot[blk][lane];
+        const f32x4 z = acc;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float m = colv ? z[r] : -INFINITY;
-                m = row16_max(m);
-                if ((lane & 15) == 0)
-                    red_m[blk][4 * (lane >> 4) + r] = m;
-            }
+        for (int r = 0; r < 4; ++r) {
+            float m = colv ? z[r] : -INFINITY;
+            m = row16_max(m);
+            if ((lane & 15) == 0)
+                red_m[blk][4 * (lane >> 4) + r] = m;
         }
         lds_barrier();
-        if (half == 0) {
+        {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * (lane >> 4) + r;
