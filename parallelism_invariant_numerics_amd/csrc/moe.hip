@@ -441,12 +441,15 @@ __device__ __forceinline__ Pipe moe_pipe(const MoeGemmArgs &a, const MoeTask &t,
     for (int i = 0; i < C::kDma; ++i)
         lds_issue_b32(ent[i], lds_addr(rows_s + C::kDma * 8 * w + 8 * i + (lane >> 3)));
     lds_wait();
+    // re-read for every task (see moe_gu_pipe_w)
+    int row_div = a.row_div;
+    asm volatile("" : "+s"(row_div));
 #pragma unroll
     for (int i = 0; i < C::kDma; ++i) {
         lds_pin(ent[i]);
         const int r = C::kDma * 8 * w + 8 * i + (lane >> 3);
         if (r < t.nvalid) {
-            const int64_t src = ent[i] / a.row_div;
+            const int64_t src = ent[i] / row_div;
             p.voffa[i] = (uint32_t)(src * a.K * 2) + c * 16;
         } else {
             p.voffa[i] = oob;
@@ -682,11 +685,17 @@ __device__ __forceinline__ PipeW moe_gu_pipe_w(const MoeGemmArgs &a, const MoeTa
     for (int i = 0; i < 4; ++i)
         lds_issue_b32(ent[i], lds_addr(rows_s + 32 * w + 8 * i + (lane >> 3)));
     lds_wait();
+    // the divisor as a value the compiler re-reads for every task: its
+    // reciprocal would otherwise be hoisted out of the task loop and spilled,
+    // and the reload waits for every memory operation, the previous task's
+    // stores included
+    int row_div = a.row_div;
+    asm volatile("" : "+s"(row_div));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         lds_pin(ent[i]);
         const int r = 32 * w + 8 * i + (lane >> 3);
-        p.voffa[i] = r < t.nvalid ? (uint32_t)((int64_t)(ent[i] / a.row_div) * a.K * 2) + c * 16
+        p.voffa[i] = r < t.nvalid ? (uint32_t)((int64_t)(ent[i] / row_div) * a.K * 2) + c * 16
                                   : oob;
     }
     const int64_t boff = static_cast<int64_t>(t.e) * a.N * a.K + t.n0 * a.K;
