@@ -275,3 +275,59 @@ def test_few_rows_match_batch(K, L, N):
             assert np.array_equal(u32(host(o)), big[start:start + m]), (m, start, "no workspace")
     check_gemm_tol(big[:16].view(np.float32), oracle.gemm(A[:16], Wt, L), absdot(A[:16], Wt),
                    f"few rows {K}/{L}")
+
+
+@pytest.mark.parametrize("K,L,M,N", [(4096, 16, 64, 4096), (4096, 16, 33, 130), (2048, 8, 128, 2048),
+                                     (4096, 64, 40, 1000), (1024, 4, 100, 203)])
+def test_split_workspace_contents_and_graph_replays(K, L, M, N):
+    """A one-partition call on few output tiles with a workspace splits K into partitions of
+    whole subtrees (roots in the workspace, then the fold).  Its bits equal the rows' bits in a
+    batch of 600 whatever the workspace held before (random bytes, all ones, the previous
+    call's roots), for FP32 and for bf16 at an odd element offset of the output, and across
+    graph replays with eager calls on the same workspace in between."""
+    t = torch()
+    A = normal_bf16(K + M, (600, K), 1.0)
+    Wt = normal_bf16(K + N + 7, (N, K), 0.02)
+    note(f"split workspace contents K={K} L={L} M={M} N={N}")
+    big = u32(_run(A, Wt, L))
+    want = big[100:100 + M]
+    wantb = f32_to_bf16_bits(want.view(np.float32))
+    c = iso.contract(L, K // L, 0)
+    a, dW = dev(A[100:100 + M]), dev(Wt)
+    need = iso.gemm_workspace(c, M, N, 1)
+    assert need > 0  # these shapes take the split
+    ws = t.randint(0, 256, (need,), dtype=t.uint8, device="cuda")
+    o = t.empty((M, N), dtype=t.float32, device="cuda")
+    ob = t.empty((M * N + 1,), dtype=t.bfloat16, device="cuda")
+    st = t.cuda.current_stream().cuda_stream
+
+    def call(out, dtype, stream=st):
+        return iso.lib.iso_gemm(ctypes.byref(c), a.data_ptr(), dW.data_ptr(), out, dtype, M, N, K,
+                                1, ws.data_ptr(), need, stream)
+
+    for fill in ("random", "again", "ones", "again"):
+        if fill == "ones":
+            ws.fill_(255)
+        o.fill_(float("nan"))
+        assert call(o.data_ptr(), iso.F32) == 0
+        t.cuda.synchronize()
+        assert np.array_equal(u32(host(o)), want), fill
+        assert call(ob.data_ptr() + 2, iso.BF16) == 0
+        t.cuda.synchronize()
+        assert np.array_equal(host(ob)[1:].view(np.uint16).reshape(M, N), wantb), fill
+
+    g = t.cuda.CUDAGraph()
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(s):
+        with t.cuda.graph(g, stream=s):
+            assert call(o.data_ptr(), iso.F32, stream=s.cuda_stream) == 0
+    t.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(u32(host(o)), want), ("replay", rep)
+        assert call(ob.data_ptr() + 2, iso.BF16) == 0  # an eager call in between
+        t.cuda.synchronize()
+        assert np.array_equal(host(ob)[1:].view(np.uint16).reshape(M, N), wantb), ("eager", rep)
