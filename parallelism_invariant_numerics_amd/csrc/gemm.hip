@@ -178,6 +178,86 @@ __global__ __launch_bounds__(256) void partition_combine4_kernel(const float *ws
     }
 }
 
+// The same fold, tile by tile, for roots written by gemm_leaf_kernel on a
+// grid of a multiple of 8 tiles: workgroup b folds rows 8 (b / ntile) ..
+// +7 of the tile that gemm_leaf_kernel's linear tile b % ntile maps to, so
+// it runs on the XCD whose L2 took that tile's roots from every partition.
+template <int P>
+__global__ __launch_bounds__(256) void partition_combine_tiles_kernel(const float *ws, void *out,
+                                                                      int64_t M, int64_t N,
+                                                                      int out_bf16)
+{
+    const int tm = static_cast<int>((M + BM - 1) / BM);
+    const int tn = static_cast<int>((N + BN - 1) / BN);
+    const int ntile = tm * tn;
+    int mt, nt;
+    xcd_tile(blockIdx.x % ntile, ntile, tn, tm, kTileGroup, nt, mt);
+    const int64_t row = static_cast<int64_t>(mt) * BM + (blockIdx.x / ntile) * 8 + (threadIdx.x >> 5);
+    const int64_t col = static_cast<int64_t>(nt) * BN + 4 * (threadIdx.x & 31);
+    if (row >= M || col >= N)
+        return;
+    const int64_t MN = M * N;
+    const int64_t e = row * N + col;
+    f32x4 v;
+    if (col + 4 <= N) {
+        f32x4 r[P];
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+            r[q] = *reinterpret_cast<const f32x4 *>(ws + q * MN + e);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ri[P];
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                ri[q] = r[q][i];
+            v[i] = fold_roots<P>(ri);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ri[P];
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                ri[q] = col + i < N ? ws[q * MN + e + i] : 0.0f;
+            v[i] = fold_roots<P>(ri);
+        }
+    }
+    const int n = col + 4 <= N ? 4 : static_cast<int>(N - col);
+    if (out_bf16) {
+        uint16_t *o = static_cast<uint16_t *>(out) + e;
+        if (n == 4) {
+            const uint32_t lo = static_cast<uint32_t>(f32_to_bf16_rne(v[0])) |
+                                (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+            const uint32_t hi = static_cast<uint32_t>(f32_to_bf16_rne(v[2])) |
+                                (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+            *reinterpret_cast<uint2 *>(o) = make_uint2(lo, hi);
+        } else {
+            for (int i = 0; i < n; ++i)
+                o[i] = f32_to_bf16_rne(v[i]);
+        }
+    } else {
+        store4_f32(static_cast<float *>(out) + e, v, n == 4, n);
+    }
+}
+
+hipError_t launch_partition_combine_tiles(const float *ws, void *out, int out_bf16, int64_t M,
+                                          int64_t N, int parts, hipStream_t stream)
+{
+    const int64_t ntile = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const bool ok = ntile % kXcds == 0 && N % 4 == 0 && reinterpret_cast<uintptr_t>(ws) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(out) % (out_bf16 ? 8 : 16) == 0;
+    if (!ok)
+        return launch_partition_combine(ws, out, out_bf16, M * N, parts, stream);
+    dim3 grid(static_cast<unsigned>(ntile * (BM / 8)));
+    switch (parts) {
+    case 2: hipLaunchKernelGGL(partition_combine_tiles_kernel<2>, grid, dim3(256), 0, stream, ws, out, M, N, out_bf16); break;
+    case 4: hipLaunchKernelGGL(partition_combine_tiles_kernel<4>, grid, dim3(256), 0, stream, ws, out, M, N, out_bf16); break;
+    case 8: hipLaunchKernelGGL(partition_combine_tiles_kernel<8>, grid, dim3(256), 0, stream, ws, out, M, N, out_bf16); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // Workgroups of at most four leaves over at least 16 stages take the
 // 128 x 256 tile when there is at least one such tile per CU (measured at
 // 4096 x 2048 x 2048 with 4 leaves: 44.1 -> 39.7 us; 4096^3 in 4 partitions:

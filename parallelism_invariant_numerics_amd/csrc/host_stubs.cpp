@@ -28,6 +28,12 @@ hipError_t launch_partition_combine(const float *, void *, int, int64_t, int, hi
     return hipErrorNotSupported;
 }
 
+hipError_t launch_partition_combine_tiles(const float *, void *, int, int64_t, int64_t, int,
+                                          hipStream_t)
+{
+    return hipErrorNotSupported;
+}
+
 hipError_t launch_lmhead_stats(const uint16_t *, const uint16_t *, const int32_t *, float *,
                                float *, float *, int64_t, int64_t, int64_t, int, int, int, int64_t,
                                int64_t, hipStream_t)

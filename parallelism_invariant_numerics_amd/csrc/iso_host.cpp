@@ -61,6 +61,12 @@ struct GemmPlan {
 
 constexpr int64_t kCus = 256;
 constexpr int64_t kSmallLayerBytes = (int64_t)8 << 20;
+// An internal split folds its roots tile by tile on the XCD that wrote them
+// while the layer's weights leave them in that XCD's L2 (measured, same bits:
+// 33-200 rows of 2048 x 2048 with 8 leaves, 2048 x 4096 with 16, 4096 x 2048
+// with 4, 3072 x 2048 with 8: 10-21 % faster; on 32 MiB of weights, 4096 x
+// 4096 or 8192 x 2048, 1-5 % slower, so those keep the element-order fold).
+constexpr int64_t kTileFoldLayerBytes = (int64_t)16 << 20;
 
 int64_t tile_count(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
@@ -334,6 +340,9 @@ iso_status iso_gemm(const iso_contract *c, const void *A, const void *Wt, void *
                                              N, K, lpp, (int)c->leaf_size, parts, st);
     if (e != hipSuccess)
         return launch_status(e);
+    if (partitions == 1 && N * K * 2 <= kTileFoldLayerBytes)
+        return launch_status(iso::launch_partition_combine_tiles(
+            static_cast<const float *>(workspace), C, bf16, M, N, parts, st));
     return launch_status(iso::launch_partition_combine(static_cast<const float *>(workspace), C,
                                                        bf16, M * N, parts, st));
 }

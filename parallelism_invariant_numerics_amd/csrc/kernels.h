@@ -31,6 +31,12 @@ hipError_t launch_gemm_rows(const uint16_t *A, const uint16_t *Wt, void *out, in
                             int64_t M, int64_t N, int64_t K, int leaves, int leaf_size,
                             hipStream_t stream);
 
+// The same over ws[parts][M][N] written by launch_gemm_partials, tile by tile
+// on the XCD that wrote each tile's roots (a grid of a multiple of 8 tiles,
+// N % 4 == 0 and aligned buffers; otherwise launch_partition_combine).
+hipError_t launch_partition_combine_tiles(const float *ws, void *out, int out_bf16, int64_t M,
+                                          int64_t N, int parts, hipStream_t stream);
+
 // out[e] = fixed tree over ws[0..parts)[e], e < MN; FP32 or bf16 output.
 hipError_t launch_partition_combine(const float *ws, void *out, int out_bf16, int64_t MN,
                                     int parts, hipStream_t stream);
