@@ -278,13 +278,17 @@ def test_few_rows_match_batch(K, L, N):
 
 
 @pytest.mark.parametrize("K,L,M,N", [(4096, 16, 64, 4096), (4096, 16, 33, 130), (2048, 8, 128, 2048),
-                                     (4096, 64, 40, 1000), (1024, 4, 100, 203)])
+                                     (4096, 64, 40, 1000), (1024, 4, 100, 203), (2048, 8, 72, 1024),
+                                     (2048, 8, 72, 1022)])
 def test_split_workspace_contents_and_graph_replays(K, L, M, N):
     """A one-partition call on few output tiles with a workspace splits K into partitions of
     whole subtrees (roots in the workspace, then the fold).  Its bits equal the rows' bits in a
     batch of 600 whatever the workspace held before (random bytes, all ones, the previous
     call's roots), for FP32 and for bf16 at an odd element offset of the output, and across
-    graph replays with eager calls on the same workspace in between."""
+    graph replays with eager calls on the same workspace in between.  The fold runs tile by tile
+    (2048 x 2048, 2048 x 1024: at most 16 MiB of weights on a multiple of 8 tiles) or in element
+    order (the rest; N = 1022 is not a multiple of 4, and a bf16 output at an odd offset is not
+    8-byte aligned)."""
     t = torch()
     A = normal_bf16(K + M, (600, K), 1.0)
     Wt = normal_bf16(K + N + 7, (N, K), 0.02)
