@@ -13,6 +13,7 @@ times, as sub-measurements reported in the JSON line:
     accumulator per logit and torch's linear + log_softmax + gather, the MoE
     block with one-leaf contracts and a plain torch expert loop scattering
     with index_add_;
+  * 64 rows of the prefill layer (K split over the workspace);
   * the sweep shape (4096 x 4096 x 4096, 16 leaves) at 1 and 8 partitions and
     at batches of 1, 8 and 64 rows; the LM-head logprob workload (8192 rows x
     2048 x 151936 vocabulary) in rows/s, fused, over 8 vocabulary shards and
@@ -401,6 +402,19 @@ def main():
     torch.cuda.synchronize()
     ok &= bool(torch.equal(out8.view(torch.int16), ref.view(torch.int16)))
     del out8, outb
+    # 64 rows of the same layer (a small batch through it): K split over the
+    # workspace and the roots folded tile by tile; rows 100.. of the batch, so
+    # the bits must match it
+    A64 = A[100:164].contiguous()
+    o64 = torch.empty((64, N), dtype=torch.bfloat16, device="cuda")
+    ws64 = torch.empty(max(1, iso.gemm_workspace(c, 64, N, 1)), dtype=torch.uint8, device="cuda")
+    a64 = _abi_gemm(iso, c, A64, W, o64, ws64, stream)
+    a64()
+    ms64 = _time_events(a64, max(10, args.steps), stream)
+    ok &= bool(torch.equal(o64.view(torch.int16), ref[100:164].view(torch.int16)))
+    extra["prefill"]["rows64_us"] = round(ms64 * 1e3, 2)
+    extra["workspace_bytes"]["prefill_rows64"] = iso.gemm_workspace(c, 64, N, 1)
+    del A64, o64, ws64
 
     if not args.quick:
         # ---------------- invariance-sweep shape, 16 leaves
